@@ -1,0 +1,138 @@
+"""Plant plausible mistakes in the oracle (on the CPU only) and check that a pin catches each.
+
+Every mutant below is a one-line slip a careful reader could make -- a dropped half-step, a
+swapped plane, '<=' for '<', the wrong midpoint, a transposed word order -- and each must make
+at least one pin of tests/test_oracle_pins.py fail."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle.loopkv_oracle as M
+from tests import test_oracle_pins as P
+
+
+def _fails(fn, *args, **kw):
+    try:
+        fn(*args, **kw)
+    except AssertionError:
+        return True
+    return False
+
+
+def _quantize_no_half(x, mn, mx, bits):
+    L = (1 << bits) - 1
+    s = O.fp16_rne((mx - mn) / L); z = O.fp16_rne(mn)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.floor((x - z) / s)
+    return np.clip(np.where(s == 0, 0, c), 0, L).astype(np.int64), s, z
+
+
+def _quantize_scale_by_levels_plus_one(x, mn, mx, bits):
+    L = (1 << bits) - 1
+    s = O.fp16_rne((mx - mn) / (L + 1)); z = O.fp16_rne(mn)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.floor((x - z) / s + 0.5)
+    return np.clip(np.where(s == 0, 0, c), 0, L).astype(np.int64), s, z
+
+
+def _planes_swapped(c):
+    c = np.asarray(c, dtype=np.int64)
+    return c & 3, c >> 2
+
+
+def _cold_midpoint_2(codes4, s, z):
+    hi = np.asarray(codes4) >> 2
+    return M._rep_v(s, codes4.shape[1]) * (4.0 * hi + 2.0) + M._rep_v(z, codes4.shape[1])
+
+
+def _mask_le(scores, m0, tau, split_tokens=0, group=32):
+    scores = np.asarray(scores, dtype=np.float64)
+    n = len(scores); hot = np.ones(n, dtype=bool); step = split_tokens or max(n, 1)
+    for s0 in range(0, n, step):
+        m = m0
+        for g0 in range(s0, min(s0 + step, n), group):
+            g1 = min(g0 + group, s0 + step, n)
+            m = max(m, float(scores[g0:g1].max()))
+            hot[g0:g1] = ~(np.exp(scores[g0:g1] - m) <= tau)
+    return hot
+
+
+def _mask_max_after_test(scores, m0, tau, split_tokens=0, group=32):
+    scores = np.asarray(scores, dtype=np.float64)
+    n = len(scores); hot = np.ones(n, dtype=bool); step = split_tokens or max(n, 1)
+    for s0 in range(0, n, step):
+        m = m0
+        for g0 in range(s0, min(s0 + step, n), group):
+            g1 = min(g0 + group, s0 + step, n)
+            with np.errstate(invalid="ignore"):
+                hot[g0:g1] = ~(np.exp(scores[g0:g1] - m) < tau)
+            m = max(m, float(scores[g0:g1].max()))
+    return hot
+
+
+def _mask_no_split_reset(scores, m0, tau, split_tokens=0, group=32):
+    return M.__dict__["_orig_fetch_mask"](scores, m0, tau, 0, group)
+
+
+def _pack_rowmajor(codes, per_word, width):
+    p, d = codes.shape
+    c = codes.astype(np.uint64).reshape(p, d // per_word, per_word)
+    return (c << (np.arange(per_word, dtype=np.uint64) * width)).sum(axis=2).astype(np.uint32)
+
+
+def _dequant_keys_sign(codes, s, z):
+    n = codes.shape[0]
+    rep = lambda a: np.repeat(a, 32, axis=0)[:n]
+    return rep(s) * codes - rep(z)
+
+
+def _attention_no_max_sub(scores, vhat):
+    # keeps the softmax but forgets to normalise by the sum
+    if np.asarray(scores).size == 0:
+        return np.zeros(vhat.shape[1])
+    p = np.exp(scores - np.max(scores))
+    return (p[:, None] * vhat).sum(0)
+
+
+def _token_bytes_no_ksz(bits, d=128, v_group=128, k_group=32):
+    r = M.__dict__["_orig_token_head_bytes"](bits, d, v_group, k_group)
+    r["ksz"] = 0.0
+    return r
+
+
+MUTANTS = {
+    "round half dropped": ("_quantize", _quantize_no_half,
+                           [P.test_quantize_matches_nearest_grid_point, P.test_quantize_ramp_closed_form], [4]),
+    "scale over 2^b levels": ("_quantize", _quantize_scale_by_levels_plus_one,
+                              [P.test_quantize_ramp_closed_form], [4]),
+    "planes swapped": ("split_planes", _planes_swapped, [P.test_planes_bijection_and_cold_error], []),
+    "cold midpoint 2": ("dequant_values_cold", _cold_midpoint_2, [P.test_planes_bijection_and_cold_error], []),
+    "cold test <=": ("fetch_mask", _mask_le, [P.test_mask_matches_non_streaming_brute_force], [0, 1.0, 0.5]),
+    "max joined after test": ("fetch_mask", _mask_max_after_test,
+                              [P.test_mask_matches_non_streaming_brute_force], [0, 0.02, -math.inf]),
+    "split ignored": ("fetch_mask", _mask_no_split_reset,
+                      [P.test_mask_matches_non_streaming_brute_force], [32, 0.02, -math.inf]),
+    "word order transposed": ("_pack_words_colmajor", _pack_rowmajor, [P.test_layout_fixture_positions], []),
+    "key zero subtracted": ("dequant_keys", _dequant_keys_sign,
+                            [P.test_quantize_error_bound], [4]),
+    "softmax unnormalised": ("attention_row", _attention_no_max_sub,
+                             [P.test_attention_special_cases], []),
+    "key scale bytes dropped": ("token_head_bytes", _token_bytes_no_ksz,
+                                [P.test_cache_bytes_match_paper_figures], []),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, mutant, pins, args = MUTANTS[name]
+    monkeypatch.setitem(M.__dict__, "_orig_fetch_mask", M.fetch_mask)
+    monkeypatch.setitem(M.__dict__, "_orig_token_head_bytes", M.token_head_bytes)
+    monkeypatch.setattr(M, attr, mutant)
+    monkeypatch.setattr(O, attr, mutant, raising=False)
+    caught = []
+    for pin in pins:
+        nargs = pin.__code__.co_argcount
+        caught.append(_fails(pin, *args[:nargs]))
+    assert any(caught), f"no pin caught mutant: {name}"

@@ -1,0 +1,376 @@
+"""Pins for the fp64 oracle: each test checks the oracle against something other than itself
+(IEEE rounding facts, closed forms, exhaustive searches, a library softmax attention, the
+paper's printed byte figures, hand-derived byte positions, stated invariants)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf16(x):
+    return torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def rand_bf16(rng, *shape, scale=1.0):
+    return bf16(rng.standard_normal(shape) * scale)
+
+
+# ------------------------------------------------------------------ fp16 rounding (IEEE 754)
+@pytest.mark.parametrize("x,bits", [
+    (1.0 / 3.0, 0x3555), (0.1, 0x2E66), (65504.0, 0x7BFF), (65520.0, 0x7C00),
+    (2.0 ** -24, 0x0001), (2.0 ** -25, 0x0000), (3 * 2.0 ** -26, 0x0001),
+    (1 + 2.0 ** -11, 0x3C00), (1 + 3 * 2.0 ** -11, 0x3C02), (-2.5, 0xC100),
+    (2.0 ** -14, 0x0400), (2.0 ** -14 - 2.0 ** -25, 0x0400),
+])
+def test_fp16_rne_ieee_values(x, bits):
+    assert int(O.fp16_bits(x)) == bits
+
+
+# ------------------------------------------------------------------ quantizer
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantize_ramp_closed_form(bits):
+    """A group whose values sit exactly on the grid z + k*s (fp16- and bf16-exact) and that
+    contains its min and max gets codes k, scale s and zero z."""
+    L = (1 << bits) - 1
+    s, z = 0.25, -1.0
+    k = np.arange(32) % (L + 1)
+    x = z + k * s
+    col = np.stack([x, x[::-1]], axis=1)              # two channels
+    codes, ks, kz = O.quantize_keys(col, bits)
+    assert np.all(ks == s) and np.all(kz == z)
+    assert np.array_equal(codes[:, 0], k) and np.array_equal(codes[:, 1], k[::-1])
+    # values: per token over one group of channels
+    row = np.tile(z + np.arange(L + 1) * s, 128 // (L + 1))[None, :]
+    vc, vs, vz = O.quantize_values(row, bits, 128)
+    assert vs[0, 0] == s and vz[0, 0] == z
+    assert np.array_equal(vc[0], np.tile(np.arange(L + 1), row.shape[1] // (L + 1)))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantize_constant_group(bits):
+    x = np.full((32, 4), bf16(0.3)[()])
+    codes, s, z = O.quantize_keys(x, bits)
+    assert np.all(s == 0) and np.all(codes == 0)
+    assert np.allclose(O.dequant_keys(codes, s, z), O.fp16_rne(x))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantize_matches_nearest_grid_point(bits):
+    """Brute force: each code is the grid point s*c + z nearest to x (ties to the upper
+    point, as round-half-up does), searched over every code."""
+    rng = np.random.default_rng(1)
+    L = (1 << bits) - 1
+    x = rand_bf16(rng, 64, 16)
+    x[:, 3] *= 10
+    codes, s, z = O.quantize_keys(x, bits)
+    sr = np.repeat(s, 32, axis=0)
+    zr = np.repeat(z, 32, axis=0)
+    grid = np.arange(L + 1)[None, None, :] * sr[..., None] + zr[..., None]
+    err = np.abs(x[..., None] - grid)
+    best = err.min(axis=-1, keepdims=True)
+    brute = np.where(err == best, np.arange(L + 1), -1).max(axis=-1)
+    assert np.array_equal(codes, brute)
+    v = rand_bf16(rng, 8, 128)
+    vc, vs, vz = O.quantize_values(v, bits, 32)
+    sr = np.repeat(vs, 32, axis=1)
+    zr = np.repeat(vz, 32, axis=1)
+    grid = np.arange(L + 1)[None, None, :] * sr[..., None] + zr[..., None]
+    err = np.abs(v[..., None] - grid)
+    best = err.min(axis=-1, keepdims=True)
+    brute = np.where(err == best, np.arange(L + 1), -1).max(axis=-1)
+    assert np.array_equal(vc, brute)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantize_error_bound(bits):
+    """|x - x^| <= s/2 away from clamping; in general within s/2 plus the fp16 rounding of
+    the group's end points."""
+    rng = np.random.default_rng(2)
+    L = (1 << bits) - 1
+    x = rand_bf16(rng, 32 * 8, 128, scale=3.0)
+    codes, s, z = O.quantize_keys(x, bits)
+    xh = O.dequant_keys(codes, s, z)
+    g = x.reshape(-1, 32, 128)
+    mn, mx = g.min(1), g.max(1)
+    slack = np.abs(mn - z) + np.abs(mx - (z + L * s))
+    bound = np.repeat(s / 2 + slack, 32, axis=0) * (1 + 1e-12)
+    assert np.all(np.abs(x - xh) <= bound)
+    assert codes.min() == 0 and codes.max() == L
+
+
+def test_quantize_fp16_subnormal_zero_point():
+    """A group minimum of 2^-25 is a tie between fp16 0 and 2^-24 and rounds to even (0)."""
+    x = np.zeros((32, 1))
+    x[:, 0] = 2.0 ** -25
+    x[5, 0] = 2.0 ** -25 + 15 * 2.0 ** -20
+    _, s, z = O.quantize_keys(x, 4)
+    assert z[0, 0] == 0.0
+    assert s[0, 0] == O.fp16_rne(2.0 ** -20)
+
+
+# ------------------------------------------------------------------ planes
+def test_planes_bijection_and_cold_error():
+    c = np.arange(16)
+    hi, lo = O.split_planes(c)
+    assert np.array_equal(4 * hi + lo, c) and hi.max() == 3 and lo.max() == 3
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 16, size=(5, 128))
+    s = O.fp16_rne(rng.uniform(0.1, 2, size=(5, 1)))
+    z = O.fp16_rne(rng.standard_normal((5, 1)))
+    full = O.dequant_values_full(codes, s, z)
+    cold = O.dequant_values_cold(codes, s, z)
+    _, lo = O.split_planes(codes)
+    assert np.allclose(cold - full, (1.5 - lo) * s, atol=0, rtol=1e-15)
+    assert np.all(np.abs(cold - full) <= 1.5 * s)
+
+
+# ------------------------------------------------------------------ mask
+def _brute_mask(scores, m0, tau, split, group=32):
+    """Non-streaming: token j's reference maximum is the seed joined with every score of its
+    split up to the end of its own group."""
+    n = len(scores)
+    step = split or n
+    hot = np.zeros(n, dtype=bool)
+    for j in range(n):
+        s0 = (j // step) * step
+        gend = min(((j - s0) // group + 1) * group + s0, s0 + step, n)
+        m = max([m0] + list(scores[s0:gend]))
+        hot[j] = math.exp(scores[j] - m) >= tau
+    return hot
+
+
+@pytest.mark.parametrize("split", [0, 32, 64, 96])
+@pytest.mark.parametrize("tau", [0.0, 0.005, 0.02, 0.3, 1.0, 2.0])
+@pytest.mark.parametrize("m0", [-math.inf, 0.5, 9.0])
+def test_mask_matches_non_streaming_brute_force(split, tau, m0):
+    rng = np.random.default_rng(4)
+    scores = rng.standard_normal(192) * 3
+    assert np.array_equal(O.fetch_mask(scores, m0, tau, split), _brute_mask(scores, m0, tau, split))
+
+
+def test_mask_identities_and_conservativeness():
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        scores = rng.standard_normal(32 * 12) * rng.uniform(0.5, 6)
+        split = [0, 32, 128, 256][trial % 4]
+        m0 = [-math.inf, float(scores.min()), float(np.median(scores))][trial % 3]
+        assert O.fetch_mask(scores, m0, 0.0, split).all()             # tau = 0: KIVI-4
+        assert not O.fetch_mask(scores, m0, 2.0, split).any()         # tau > 1: hi only
+        prev = None
+        for tau in [0.001, 0.01, 0.05, 0.2, 0.9]:
+            hot = O.fetch_mask(scores, m0, tau, split)
+            # Proposition 1: the running max never exceeds the row max (seed <= row max
+            # here), so every cold token's weight is below tau times the row's largest.
+            p = np.exp(scores - scores.max())
+            assert np.all(p[~hot] < tau)
+            if prev is not None:
+                assert np.all(hot <= prev)                          # monotone in tau
+            prev = hot
+    scores = rng.standard_normal(96)
+    assert np.array_equal(O.fetch_mask(scores, -math.inf, 0.05, 0),
+                          O.fetch_mask(scores, -math.inf, 0.05, 4096))
+
+
+# ------------------------------------------------------------------ attention
+def _sdpa(q, k, v):
+    """torch's scaled-dot-product attention in float64 (library routine, default 1/sqrt(D))."""
+    t = lambda a: torch.as_tensor(a, dtype=torch.float64)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q)[:, :, None], t(k), t(v))[0, 0, 0].numpy()
+
+
+def _head(rng, n, bits, v_group=128, d=128, outliers=True):
+    k = rand_bf16(rng, n, d)
+    if outliers:
+        k[:, rng.choice(d, 4, replace=False)] *= 10
+    v = rand_bf16(rng, n, d)
+    return k, v, O.quantize_head(k, v, bits, v_group)
+
+
+@pytest.mark.parametrize("bits,tau", [(4, 0.0), (4, 2.0), (2, 0.01), (2, 0.0)])
+@pytest.mark.parametrize("v_group", [128, 32])
+def test_attention_reduces_to_library_sdpa(bits, tau, v_group):
+    """tau = 0 on INT4 is full INT4 attention; tau > 1 is hi-only attention; INT2 has no
+    mask. Each equals a library softmax attention over the dequantized keys and values,
+    with the exact bf16 tail appended."""
+    rng = np.random.default_rng(6)
+    _, _, qh = _head(rng, 96, bits, v_group)
+    q = rand_bf16(rng, 128)
+    tk, tv = rand_bf16(rng, 7, 128), rand_bf16(rng, 7, 128)
+    out, hot, _ = O.decode_head(q, qh, tk, tv, sm_scale=1 / math.sqrt(128), tau=tau)
+    khat = O.dequant_keys(qh.k_codes, qh.k_s, qh.k_z)
+    if bits == 4 and tau > 1:
+        vhat = O.dequant_values_cold(qh.v_codes, qh.v_s, qh.v_z)
+        assert not hot.any()
+    else:
+        vhat = O.dequant_values_full(qh.v_codes, qh.v_s, qh.v_z)
+        assert hot.all()
+    ref = _sdpa(q, np.concatenate([khat, tk]), np.concatenate([vhat, tv]))
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(7)
+    _, _, qh = _head(rng, 32, 4)
+    # a single exact token: the output is that token's value
+    v1 = rand_bf16(rng, 1, 128)
+    out, _, _ = O.decode_head(rand_bf16(rng, 128), None, rand_bf16(rng, 1, 128), v1,
+                              sm_scale=0.1, tau=0.01)
+    assert np.allclose(out, v1[0], rtol=0, atol=1e-15)
+    # zero query: every score is 0, every token hot (exp(0) = 1 >= tau), output = mean
+    out, hot, _ = O.decode_head(np.zeros(128), qh, np.zeros((0, 128)), np.zeros((0, 128)),
+                                sm_scale=0.1, tau=0.5)
+    assert hot.all()
+    assert np.allclose(out, O.dequant_values_full(qh.v_codes, qh.v_s, qh.v_z).mean(0), rtol=1e-13)
+    # empty row: zeros by definition
+    out, _, _ = O.decode_head(np.ones(128), None, np.zeros((0, 128)), np.zeros((0, 128)),
+                              sm_scale=0.1, tau=0.5)
+    assert np.all(out == 0)
+
+
+@pytest.mark.parametrize("v_group", [128, 32])
+def test_proposition1_error_bound(v_group):
+    """Weights are those of the full INT4 reader; a cold token moves the output by at most
+    1.5 * s * p_j per channel."""
+    rng = np.random.default_rng(8)
+    _, _, qh = _head(rng, 256, 4, v_group)
+    q = rand_bf16(rng, 128)
+    sm = 1 / math.sqrt(128)
+    o0, _, s0 = O.decode_head(q, qh, np.zeros((0, 128)), np.zeros((0, 128)), sm_scale=sm, tau=0.0)
+    for tau in [0.005, 0.02, 0.2, 2.0]:
+        ot, hot, st = O.decode_head(q, qh, np.zeros((0, 128)), np.zeros((0, 128)), sm_scale=sm, tau=tau)
+        assert np.array_equal(s0, st)
+        p = np.exp(st - st.max()); p /= p.sum()
+        sch = np.repeat(qh.v_s, v_group, axis=1)                  # [n, D]
+        bound = 1.5 * ((~hot)[:, None] * p[:, None] * sch).sum(0)
+        assert np.all(np.abs(ot - o0) <= bound * (1 + 1e-9) + 1e-15)
+        assert (~hot).sum() > 0
+
+
+def test_split_invariance_at_identity_taus():
+    rng = np.random.default_rng(9)
+    _, _, qh = _head(rng, 256, 4)
+    q = rand_bf16(rng, 128)
+    e = np.zeros((0, 128))
+    for tau in [0.0, 2.0]:
+        outs = [O.decode_head(q, qh, e, e, sm_scale=0.09, tau=tau, split_tokens=s)[0]
+                for s in [0, 32, 64, 160]]
+        for o in outs[1:]:
+            assert np.array_equal(o, outs[0])
+
+
+# ------------------------------------------------------------------ layout
+def test_layout_fixture_positions():
+    fx = json.load(open(os.path.join(GOLDEN, "layout_single_codes.json")))
+    for case in fx["cases"]:
+        if "sizes" in case:
+            for key, size in case["sizes"].items():
+                bits = 4 if key.startswith("int4") else 2
+                p = int(key.split("_")[1][1:])
+                g = int(key.split("_")[2][1:])
+                assert O.head_block_layout(bits, p, 128, g)["total"][1] == size
+            continue
+        P, bits = case["page_tokens"], case["bits"]
+        kc = np.zeros((P, 128), dtype=np.int64)
+        vc = np.zeros((P, 128), dtype=np.int64)
+        (kc if case["tensor"] == "k" else vc)[case["token"], case["channel"]] = case["code"]
+        buf = O.pack_head_block(bits, P, kc, vc, np.zeros((P, 1)), np.zeros((P, 1)))
+        expect = case.get("bytes", [[case.get("byte"), case.get("value")]])
+        nz = {int(i): int(buf[i]) for i in np.nonzero(buf)[0]}
+        assert nz == {b: v for b, v in expect}, case["what"]
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("P", [16, 32])
+@pytest.mark.parametrize("v_group", [128, 32])
+def test_layout_round_trip(bits, P, v_group):
+    rng = np.random.default_rng(10)
+    L = (1 << bits) - 1
+    kc = rng.integers(0, L + 1, size=(P, 128))
+    vc = rng.integers(0, L + 1, size=(P, 128))
+    nvg = 128 // v_group
+    vs, vz = O.fp16_rne(rng.uniform(0, 1, (P, nvg))), O.fp16_rne(rng.standard_normal((P, nvg)))
+    ks, kz = O.fp16_rne(rng.uniform(0, 1, 128)), O.fp16_rne(rng.standard_normal(128))
+    buf = O.pack_head_block(bits, P, kc, vc, vs, vz, ks, kz, v_group)
+    u = O.unpack_head_block(bits, P, buf, 128, v_group)
+    assert np.array_equal(u["k_codes"], kc) and np.array_equal(u["v_codes"], vc)
+    assert np.array_equal(u["v_s"], vs) and np.array_equal(u["v_z"], vz)
+    assert np.array_equal(u["k_s"], ks) and np.array_equal(u["k_z"], kz)
+
+
+@pytest.mark.parametrize("P", [16, 32])
+def test_page_table_invariance(P):
+    """Packing a history into pages through a shuffled table and reading it back gives
+    the same quantized history, hence the same output."""
+    rng = np.random.default_rng(11)
+    H = 2
+    heads = [[_head(rng, 96, 4)[2] for _ in range(H)] for _ in range(2)]
+    n_lp = 96 // P
+    perm = rng.permutation(2 * n_lp).reshape(2, n_lp)
+    pool = O.pack_pool(4, P, heads, perm, 2 * n_lp)
+    q = rand_bf16(rng, 128)
+    for b in range(2):
+        for h in range(H):
+            back = O.unpack_pool_head(4, P, pool, perm[b], 96, h, H)
+            for f in ["k_codes", "k_s", "k_z", "v_codes", "v_s", "v_z"]:
+                assert np.array_equal(getattr(back, f), getattr(heads[b][h], f))
+            o1 = O.decode_head(q, back, np.zeros((0, 128)), np.zeros((0, 128)), sm_scale=.09, tau=.01)[0]
+            o2 = O.decode_head(q, heads[b][h], np.zeros((0, 128)), np.zeros((0, 128)), sm_scale=.09, tau=.01)[0]
+            assert np.array_equal(o1, o2)
+
+
+# ------------------------------------------------------------------ byte model
+def _plan(name, layers, loops):
+    p = np.full((loops, layers), 4, dtype=np.uint8)
+    if name == "int4_loop3_reuse":
+        p[2, :] = 0
+    elif name == "int2_loops123":
+        p[:3, :] = 2
+    elif name == "loopkv_r":          # 25 of the 72 history cells INT2, in the first/last 6 layers
+        cells = [(t, l) for t in range(3) for l in list(range(6)) + list(range(18, 24))]
+        for t, l in cells[:25]:
+            p[t, l] = 2
+    elif name == "loopkv_m":          # 26 shared, 20 own INT2, 50 INT4 (loop 4 all INT4)
+        flat = [(t, l) for t in range(3) for l in range(layers)]
+        for t, l in flat[:26]:
+            p[t, l] = 0
+        for t, l in flat[26:46]:
+            p[t, l] = 2
+    return p
+
+
+def test_cache_bytes_match_paper_figures():
+    fx = json.load(open(os.path.join(GOLDEN, "page_kib_per_token.json")))
+    for c in fx["cases"]:
+        if c["plan"] == "bf16":
+            assert O.bf16_bytes_per_token(c["layers"] * c["loops"]) / 1024 == c["stored"]
+            continue
+        r = O.cache_bytes_ref(_plan(c["plan"], c["layers"], c["loops"]), 16, 128, 32)
+        assert r["stored"] / 1024 == c["stored"], c["name"]
+        if "read" in c:
+            assert r["read_all_hot"] / 1024 == c["read"], c["name"]
+    vp = fx["v_precision"]
+    lo, hi = vp["full_precision_fraction_range"]
+    for name in ["loopkv_r", "loopkv_m"]:
+        r = O.cache_bytes_ref(_plan(name, 24, 4), 16, 128, 32)
+        n_int4_read = (r["read_all_hot"] - r["read_hi_only"]) / 1024 / vp["lo_plane_kib_per_token_and_layer"]
+        assert n_int4_read == int(n_int4_read)
+        read = lambda f: (r["read_hi_only"] + f * (r["read_all_hot"] - r["read_hi_only"])) / 1024
+        assert read(lo) <= vp[name]["read_with_v_precision"] + 0.5
+        assert read(hi) >= vp[name]["read_with_v_precision"] - 0.5
+
+
+def test_cache_bytes_baseline_shapes():
+    """128-channel value groups: 148 B per INT4 (token, head), 84 B per INT2."""
+    assert sum(O.token_head_bytes(4).values()) == 148
+    assert sum(O.token_head_bytes(2).values()) == 84
+    r = O.cache_bytes_ref(np.array([[4], [2], [0], [4]], dtype=np.uint8))
+    assert r["stored"] == 16 * (148 + 84 + 148)
+    assert r["read_all_hot"] == 16 * (148 + 84 + 148 + 148)
+    assert r["read_all_hot"] - r["read_hi_only"] == 16 * 32 * 3
