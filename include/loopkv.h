@@ -1,0 +1,200 @@
+/*
+ * loopkv.h -- C ABI of libloopkv: LoopKV's fused decode attention and its companion
+ * quantize-append step, for one AMD Instinct MI355X (gfx950).
+ *
+ * Source of the operations: "Loop-Aware KV Cache Compression for Serving Looped
+ * Transformers" (the LoopKV paper).
+ *   - A cell is one (loop, layer) pair of a looped transformer; a plan gives each cell one
+ *     storage option: 4-bit codes, 2-bit codes, or reuse of the final loop's KV at the same
+ *     layer (section 3, "System Design"; section 3.1 C1; section 3.2 C2).
+ *   - An INT4 cell stores values as a high and a low 2-bit plane; attention reads the high
+ *     plane of every token and the low plane only for tokens whose weight reaches tau times
+ *     a running maximum seeded by m0 (section 3.3 C3, "Read-time V precision").
+ *   - One launch per cell reads its history pages through a per-cell descriptor built at plan
+ *     load; split partials merge by log-sum-exp (section 3.4, "One launch per cell").
+ *   - KIVI-style quantization (section 5.1, "Baselines"): keys per channel over a 32-token
+ *     page, values per token over groups of channels, asymmetric, fp16 scale and zero point.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are device pointers; all others are host pointers.
+ *   - The caller owns every device buffer (arena, q, out, k_new, v_new, seq_lens, page
+ *     table, seed, mask, stats). The library never allocates device memory; after
+ *     loopkv_plan_load it only launches kernels and enqueues copies on the given stream, with
+ *     no host synchronisation, so appends and decodes can be captured in a HIP graph.
+ *   - Streams are hipStream_t passed as void*; NULL is the default stream.
+ *   - Errors are status codes; nothing is thrown across the ABI. Host-side arguments are
+ *     validated before anything is enqueued: on any status other than LOOPKV_OK nothing has
+ *     been launched. Values that live in device memory (lengths, page ids) cannot be checked
+ *     on the host; kernels clamp them and record a flag readable with loopkv_device_errors.
+ *   - A plan handle is not thread-safe; calls on different handles are independent.
+ *   - loop and layer are 0-based; the final loop is num_loops - 1.
+ */
+#ifndef LOOPKV_H
+#define LOOPKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct loopkv_plan_s* loopkv_plan; /* opaque; host memory owned by the library */
+
+typedef enum {
+  LOOPKV_OK = 0,
+  LOOPKV_EINVAL = 1,    /* bad argument: null pointer, index or size out of range */
+  LOOPKV_EPLAN = 2,     /* bad plan table: unknown code, or REUSE in the final loop */
+  LOOPKV_ENOTSUP = 3,   /* a shape this build does not implement */
+  LOOPKV_ECAPACITY = 4, /* arena smaller than loopkv_cache_bytes says, or a split count
+                           above shape.max_splits */
+  LOOPKV_EHIP = 5       /* a HIP runtime call or kernel launch failed */
+} loopkv_status;
+
+/* Plan codes, one uint8 per cell, indexed plan[loop * num_layers + layer]. */
+enum { LOOPKV_REUSE = 0, LOOPKV_INT2 = 2, LOOPKV_INT4 = 4 };
+
+/* Static shape of a cache. The key group is fixed at 32 tokens (one page of the paper);
+ * a page of 16 tokens makes two pages per key group. */
+typedef struct {
+  int32_t num_layers;        /* L >= 1 */
+  int32_t num_loops;         /* T >= 1 */
+  int32_t num_kv_heads;      /* H >= 1 */
+  int32_t num_q_heads;       /* must equal num_kv_heads (no grouped-query attention) */
+  int32_t head_dim;          /* D; this build supports 128 */
+  int32_t page_tokens;       /* tokens per physical page: 16 or 32 */
+  int32_t v_group;           /* value channels per scale/zero: 32, 64 or 128 */
+  int32_t max_batch;         /* requests per call, at most */
+  int32_t max_pages_per_seq; /* page-table row capacity; context <= this * page_tokens */
+  int32_t tail_tokens;       /* exact bf16 ring per (cell, request) for tokens not yet
+                                quantized: 32..1024, a multiple of 32 (64 recommended) */
+  int32_t max_splits;        /* split-K partials per row the workspace holds (>= 1) */
+  int32_t reserved;          /* set to 0 */
+  int64_t num_pages;         /* physical pages in each own-storage cell's pool */
+} loopkv_shape;
+
+/* Sizes, in bytes. The arena is: metadata | workspace | tails | pools. */
+typedef struct {
+  uint64_t arena_bytes;      /* total device bytes loopkv_plan_load needs */
+  uint64_t pool_bytes;       /* page pools of all own-storage cells */
+  uint64_t tail_bytes;       /* bf16 tail rings of all cells (REUSE cells keep their own) */
+  uint64_t meta_bytes;       /* descriptors, quantized-group counters, error word */
+  uint64_t workspace_bytes;  /* split-K partials */
+  /* Bytes per token summed over every cell and head (algorithmic, excluding pool padding):
+   * stored -- quantized KV kept (REUSE cells keep none);
+   * read_hi_only / read_all_hot -- what one decode step reads per history token when no /
+   * every low plane is fetched (a REUSE cell reads its source's bytes). */
+  double stored_bytes_per_token;
+  double read_bytes_per_token_hi_only;
+  double read_bytes_per_token_all_hot;
+} loopkv_bytes;
+
+/* Per-call decode options. */
+typedef struct {
+  float tau;                  /* V-precision threshold; 0 fetches every low plane, > 1 none */
+  float sm_scale;             /* score scale; 0 means 1/sqrt(head_dim) */
+  int32_t split_tokens;       /* 0: one split per (request, head) row; otherwise a multiple
+                                 of 32: the history is cut into runs of this many tokens
+                                 from token 0, each with its own running maximum, merged by
+                                 log-sum-exp in split order */
+  int32_t mask_stride;        /* row stride of fetch_mask_dev, in bytes */
+  const float* seed_dev;      /* [batch, num_q_heads] running-max seeds in score units, or
+                                 NULL for -infinity */
+  uint8_t* fetch_mask_dev;    /* optional [batch, num_q_heads, mask_stride]: per history
+                                 token, 1 if its low plane was read (hot), 0 if not (cold);
+                                 1 for every history token of a cell read at 2 bits; tail
+                                 entries are not written. NULL to skip. */
+  unsigned long long* stats_dev; /* optional [4] counters, accumulated (not reset):
+                                 [0] history (token, head) pairs read, [1] of those, pairs
+                                 whose low plane was read, [2] pairs read from INT4 pools,
+                                 [3] tail (token, head) pairs. NULL to skip. */
+} loopkv_decode_opts;
+
+/* Device view of one cell, for inspection by callers and tests. */
+typedef struct {
+  int32_t code;               /* the plan code of this cell */
+  int32_t read_bits;          /* bits of the pool this cell reads (the source's for REUSE) */
+  int32_t gated;              /* 1 if the low plane is fetched only for hot tokens */
+  int32_t head_block_bytes;   /* bytes of one head of one page */
+  int64_t page_bytes;         /* num_kv_heads * head_block_bytes */
+  void* read_pool_dev;        /* pool this cell reads (own, or the final loop's) */
+  void* own_pool_dev;         /* pool this cell writes; NULL for REUSE */
+  void* tail_k_dev;           /* bf16 [max_batch, tail_tokens, H, D] ring, slot = pos % tail */
+  void* tail_v_dev;
+  int32_t* qgroups_dev;       /* int32 [max_batch]: 32-token groups quantized so far (own
+                                 storage only; a REUSE cell reads its source's) */
+} loopkv_cell_info;
+
+/* Sizes of the arena for `shape` and `plan` (num_loops * num_layers codes), and the
+ * stored / read bytes per token. Pure host computation; no HIP call. */
+loopkv_status loopkv_cache_bytes(const loopkv_shape* shape, const uint8_t* plan,
+                                 loopkv_bytes* out);
+
+/* Builds one descriptor per cell (section 3.4) in the caller's device arena and returns a
+ * handle. The arena must hold at least loopkv_cache_bytes().arena_bytes bytes and be
+ * 256-byte aligned. Counters and the error word are zeroed on `stream`; pools and tails are
+ * not touched (their contents are defined only where appends wrote them). The plan table
+ * is copied; `plan` may be freed after the call. */
+loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan,
+                               void* arena_dev, uint64_t arena_bytes, void* stream,
+                               loopkv_plan* out);
+
+/* Releases the handle (host memory only; the arena stays the caller's). NULL is a no-op. */
+loopkv_status loopkv_plan_free(loopkv_plan plan);
+
+/* Appends new tokens to every request of cell (layer, loop).
+ *   k_new_dev, v_new_dev: bf16 [batch, n_new, num_kv_heads, head_dim], contiguous.
+ *   n_new_dev: optional int32 [batch]: request b appends its first n_new_dev[b] rows
+ *   (0 <= n_new_dev[b] <= n_new); NULL appends all n_new rows of every request.
+ *   seq_lens_dev: int32 [batch], tokens each request held before this append.
+ *   page_table_dev: int32 [batch, page_table_stride], logical page -> physical page id in
+ *   [0, num_pages); one table serves every cell.
+ * With m = the request's appended count, its last min(m, tail_tokens) tokens enter the
+ * cell's bf16 ring. For an own-storage cell, every 32-token key group the append completes is
+ * quantized into the cell's pool (KIVI-style, fp16 scale/zero, INT4 values split into hi/lo
+ * planes) and the cell's quantized-group counter becomes floor((seq_len + m) / 32). A REUSE
+ * cell only fills its ring: its history is the final loop's pool, as far as that cell's
+ * counter says. n_new == 0 is a no-op. Precondition (device data): the tokens of a group
+ * completed by this call that precede it are still in the ring, i.e. every earlier append of
+ * the request also ran. */
+loopkv_status loopkv_quantize_append(loopkv_plan plan, int32_t layer, int32_t loop,
+                                     const void* k_new_dev, const void* v_new_dev,
+                                     int32_t batch, int32_t n_new,
+                                     const int32_t* n_new_dev,
+                                     const int32_t* seq_lens_dev,
+                                     const int32_t* page_table_dev,
+                                     int32_t page_table_stride, void* stream);
+
+/* Decode attention of cell (layer, loop) for one query token per request.
+ *   q_dev: bf16 [batch, num_q_heads, head_dim]; out_dev: fp32 [batch, num_q_heads, head_dim].
+ *   seq_lens_dev: int32 [batch], context length including the newest token.
+ * History = the first 32*g tokens, g = min(source counter, seq_len / 32), read from the
+ * pool the cell's descriptor names; tail = the remaining tokens, read exactly from the
+ * cell's own ring (at most tail_tokens of them). Scores are sm_scale * q . k^; softmax over
+ * history and tail; history values of an INT4 pool decode at full precision for hot tokens
+ * and to the middle of their high-plane bucket for cold ones (section 3.3). A request with
+ * seq_len 0 gets zeros. opts may be NULL (tau 0, default scale, no split). */
+loopkv_status loopkv_decode_attention(loopkv_plan plan, int32_t layer, int32_t loop,
+                                      const void* q_dev, int32_t batch,
+                                      const int32_t* seq_lens_dev,
+                                      const int32_t* page_table_dev,
+                                      int32_t page_table_stride,
+                                      const loopkv_decode_opts* opts, float* out_dev,
+                                      void* stream);
+
+/* Fills `out` with the device view of cell (layer, loop). Host only. */
+loopkv_status loopkv_get_cell_info(loopkv_plan plan, int32_t layer, int32_t loop,
+                                   loopkv_cell_info* out);
+
+/* Waits for `stream`, then returns in *flags the OR of the device-side flags kernels raised
+ * since the last call, and clears them: 1 = a length out of range, 2 = a page id out of
+ * range, 4 = more tail tokens than the ring holds. */
+loopkv_status loopkv_device_errors(loopkv_plan plan, void* stream, uint32_t* flags);
+
+/* Static string naming a status. */
+const char* loopkv_status_string(loopkv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOOPKV_H */

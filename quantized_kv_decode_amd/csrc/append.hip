@@ -1,0 +1,276 @@
+// Quantize-append: the companion step that moves new tokens into a cell's storage.
+//
+// "Loop-Aware KV Cache Compression for Serving Looped Transformers": a 32-token page is
+// quantized into its cell's pool when it leaves the exact window (section 2.3; section 4,
+// "vLLM integration"); KIVI-style asymmetric quantization, keys per channel over the page,
+// values per token over channel groups (section 5.1, "Baselines"); an INT4 cell stores its
+// value codes as a high and a low 2-bit plane (section 3.3, "Bit-plane V layout"). Here a
+// group is quantized by the append that completes it, and the newest tokens stay exact in
+// a per-(cell, request) bf16 ring until then.
+//
+// Rounding (bit-exact by construction): scale = fp16_rne((max - min) / (2^b - 1)) and
+// zero = fp16_rne(min), each rounded once from a double; code = clamp(floor((x - zero) /
+// scale + 1/2), 0, 2^b - 1) in double precision; a zero scale gives code 0.
+#include "loopkv_internal.h"
+
+namespace loopkv {
+namespace {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Round a double to the nearest fp16 (ties to even) and return its bits. One rounding,
+// straight from the double's significand.
+__device__ uint16_t f64_to_f16_bits(double x) {
+  const uint64_t bits = (uint64_t)__double_as_longlong(x);
+  const uint32_t sign = (uint32_t)(bits >> 48) & 0x8000u;
+  const int exp = (int)((bits >> 52) & 0x7FF);
+  const uint64_t mant = bits & ((1ull << 52) - 1);
+  if (exp == 0x7FF) return (uint16_t)(sign | 0x7C00u | (mant ? 0x200u : 0u));
+  if (exp == 0) return (uint16_t)sign;  // double subnormals are far below fp16's range
+  const uint64_t sig = (1ull << 52) | mant;  // value = sig * 2^(exp - 1075)
+  int e = exp - 1023 + 15;                   // biased fp16 exponent if normal
+  int shift = e >= 1 ? 42 : 42 + (1 - e);    // bits dropped from sig
+  if (shift > 53) return (uint16_t)sign;     // below half the smallest subnormal
+  uint64_t m = sig >> shift;
+  const uint64_t rem = sig & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (m & 1))) ++m;
+  if (e >= 1) {
+    if (m == (1ull << 11)) { m >>= 1; ++e; }
+    if (e >= 31) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | ((uint32_t)e << 10) | (uint32_t)(m & 0x3FF));
+  }
+  return (uint16_t)(sign | (uint32_t)m);  // subnormal; m == 0x400 is the smallest normal
+}
+
+__device__ double f16_bits_to_f64(uint16_t h) {
+  const int e = (h >> 10) & 0x1F;
+  const int m = h & 0x3FF;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);
+  else if (e == 31) v = m ? __longlong_as_double(0x7FF8000000000000ll) : __longlong_as_double(0x7FF0000000000000ll);
+  else v = ldexp((double)(1024 + m), e - 25);
+  return (h & 0x8000) ? -v : v;
+}
+
+__device__ __forceinline__ int quant_code(double x, double s, double z, int levels) {
+  if (s == 0.0) return 0;
+  double c = floor((x - z) / s + 0.5);
+  c = c < 0.0 ? 0.0 : (c > (double)levels ? (double)levels : c);
+  return (int)c;
+}
+
+__device__ __forceinline__ void raise_error(uint32_t* err, uint32_t flag) { atomicOr(err, flag); }
+
+// One workgroup of 128 threads quantizes one completed 32-token key group of one
+// (request, head) into the cell's pool. blockIdx = (group index within this call, head,
+// request).
+// Tokens request b appends in this call: n_new_dev[b] if given (clamped to [0, n_new]).
+__device__ __forceinline__ int appended(const int32_t* n_new_dev, int n_new, int b) {
+  if (!n_new_dev) return n_new;
+  const int m = n_new_dev[b];
+  return m < 0 ? 0 : (m > n_new ? n_new : m);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(128) void quantize_group_kernel(
+    Geom g, const CellDesc* __restrict__ descp, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, int n_new, const int32_t* __restrict__ n_new_dev,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int pt_stride) {
+  constexpr int L = (1 << BITS) - 1;
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const CellDesc& d = *descp;
+  const int old = seq_lens[b];
+  const int64_t nw = (int64_t)old + appended(n_new_dev, n_new, b);
+  const int64_t cap = min((int64_t)g.max_ctx, (int64_t)pt_stride * g.P);
+  if (old < 0 || nw > cap) {
+    if (blockIdx.x == 0 && h == 0 && tid == 0) raise_error(g.err, kErrLength);
+    return;
+  }
+  if (n_new_dev && (n_new_dev[b] < 0 || n_new_dev[b] > n_new) && blockIdx.x == 0 && h == 0 && tid == 0)
+    raise_error(g.err, kErrLength);
+  const int grp = old / kGroup + (int)blockIdx.x;
+  if ((int64_t)(grp + 1) * kGroup > nw) return;
+
+  __shared__ float ks[kGroup][kHeadDim + 1];
+  __shared__ float vs[kGroup][kHeadDim + 1];
+  __shared__ uint8_t kcode[kGroup][kHeadDim];
+  __shared__ uint8_t vcode[kGroup][kHeadDim];
+  __shared__ uint32_t vsz[kGroup][4];
+  __shared__ int64_t page_base[kGroup / 16];
+
+  const int H = g.H, D = g.D;
+  // Stage the group's 32 tokens: positions before `old` come from the ring, later ones
+  // from this call's input. Each wave reads whole 256-byte rows.
+  for (int t = 0; t < kGroup; ++t) {
+    const int pos = grp * kGroup + t;
+    const uint16_t *kp, *vp;
+    if (pos >= old) {
+      const size_t row = ((size_t)b * n_new + (pos - old)) * H + h;
+      kp = k_new + row * D;
+      vp = v_new + row * D;
+    } else {
+      const size_t row = ((size_t)b * g.tail + (pos % g.tail)) * H + h;
+      kp = d.tail_k + row * D;
+      vp = d.tail_v + row * D;
+    }
+    ks[t][tid] = bf16_to_f32(kp[tid]);
+    vs[t][tid] = bf16_to_f32(vp[tid]);
+  }
+  // Physical pages holding the group (one for 32-token pages, two for 16-token pages).
+  if (tid < kGroup / g.P) {
+    const int lp = grp * kGroup / g.P + tid;
+    const int pid = page_table[(size_t)b * pt_stride + lp];
+    if (pid < 0 || pid >= g.num_pages) {
+      raise_error(g.err, kErrPage);
+      page_base[tid] = -1;
+    } else {
+      page_base[tid] = (int64_t)pid * d.own_page_bytes;
+    }
+  }
+  __syncthreads();
+  for (int i = 0; i < kGroup / g.P; ++i)
+    if (page_base[i] < 0) return;
+
+  const Layout lay = head_layout(BITS, g.P, D, g.nvg);
+  const int64_t hoff = (int64_t)h * lay.total;
+
+  // Keys: thread = channel; min/max over the group's tokens.
+  {
+    const int c = tid;
+    double mn = ks[0][c], mx = mn;
+    for (int t = 1; t < kGroup; ++t) {
+      const double x = ks[t][c];
+      mn = x < mn ? x : mn;
+      mx = x > mx ? x : mx;
+    }
+    const uint16_t sb = f64_to_f16_bits((mx - mn) / (double)L);
+    const uint16_t zb = f64_to_f16_bits(mn);
+    const double s = f16_bits_to_f64(sb), z = f16_bits_to_f64(zb);
+    for (int t = 0; t < kGroup; ++t) kcode[t][c] = (uint8_t)quant_code(ks[t][c], s, z, L);
+    uint8_t* blk = d.own_pool + page_base[0] + hoff;
+    reinterpret_cast<uint32_t*>(blk + lay.ksz)[c] = (uint32_t)sb | ((uint32_t)zb << 16);
+  }
+  // Values: four threads per token, 32 channels each; groups wider than 32 channels
+  // combine their min/max across neighbouring lanes.
+  {
+    const int t = tid >> 2, part = tid & 3, c0 = part * 32;
+    double mn = vs[t][c0], mx = mn;
+    for (int c = 1; c < 32; ++c) {
+      const double x = vs[t][c0 + c];
+      mn = x < mn ? x : mn;
+      mx = x > mx ? x : mx;
+    }
+    for (int w = 1; w < g.v_group / 32; w <<= 1) {
+      const double omn = __shfl_xor(mn, w), omx = __shfl_xor(mx, w);
+      mn = omn < mn ? omn : mn;
+      mx = omx > mx ? omx : mx;
+    }
+    const uint16_t sb = f64_to_f16_bits((mx - mn) / (double)L);
+    const uint16_t zb = f64_to_f16_bits(mn);
+    const double s = f16_bits_to_f64(sb), z = f16_bits_to_f64(zb);
+    for (int c = 0; c < 32; ++c) vcode[t][c0 + c] = (uint8_t)quant_code(vs[t][c0 + c], s, z, L);
+    if (c0 % g.v_group == 0) vsz[t][c0 / g.v_group] = (uint32_t)sb | ((uint32_t)zb << 16);
+  }
+  __syncthreads();
+
+  // Pack words and store them into the page(s).
+  auto tok_block = [&](int t, int* tl) -> uint8_t* {
+    const int pos_in_grp = t;
+    const int pi = pos_in_grp / g.P;
+    *tl = pos_in_grp % g.P;
+    return d.own_pool + page_base[pi] + hoff;
+  };
+  constexpr int KPW = 32 / BITS;  // key channels per word
+  for (int w = tid; w < (kHeadDim / KPW) * kGroup; w += 128) {
+    const int cb = w / kGroup, t = w % kGroup;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) word |= (uint32_t)kcode[t][cb * KPW + i] << (BITS * i);
+    int tl;
+    uint8_t* blk = tok_block(t, &tl);
+    reinterpret_cast<uint32_t*>(blk + lay.kc)[cb * g.P + tl] = word;
+  }
+  for (int w = tid; w < (kHeadDim / 16) * kGroup; w += 128) {
+    const int cb = w / kGroup, t = w % kGroup;
+    uint32_t hiw = 0, low = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t c = vcode[t][cb * 16 + i];
+      if (BITS == 4) {
+        hiw |= (c >> 2) << (2 * i);
+        low |= (c & 3u) << (2 * i);
+      } else {
+        hiw |= c << (2 * i);
+      }
+    }
+    int tl;
+    uint8_t* blk = tok_block(t, &tl);
+    reinterpret_cast<uint32_t*>(blk + lay.vc)[cb * g.P + tl] = hiw;
+    if (BITS == 4) reinterpret_cast<uint32_t*>(blk + lay.vlo)[tl * (kHeadDim / 16) + cb] = low;
+  }
+  for (int w = tid; w < kGroup * g.nvg; w += 128) {
+    const int t = w / g.nvg, vg = w % g.nvg;
+    int tl;
+    uint8_t* blk = tok_block(t, &tl);
+    reinterpret_cast<uint32_t*>(blk + lay.vsz)[tl * g.nvg + vg] = vsz[t][vg];
+  }
+}
+
+// Copies the last min(n_new, tail) new tokens of each request into the cell's ring and, for
+// an own-storage cell, sets its quantized-group counter. blockIdx = (chunk, request).
+__global__ __launch_bounds__(256) void tail_write_kernel(
+    Geom g, const CellDesc* __restrict__ descp, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, int n_new, const int32_t* __restrict__ n_new_dev,
+    const int32_t* __restrict__ seq_lens, int pt_stride) {
+  const CellDesc& d = *descp;
+  const int b = blockIdx.y;
+  const int old = seq_lens[b];
+  const int m = appended(n_new_dev, n_new, b);
+  const int64_t nw = (int64_t)old + m;
+  const int64_t cap = min((int64_t)g.max_ctx, (int64_t)pt_stride * g.P);
+  if (old < 0 || nw > cap) return;  // flagged by the quantize kernel
+  const int first = m > g.tail ? m - g.tail : 0;
+  const int chunks_per_tok = g.H * g.D / 8;  // 16-byte chunks per token
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)(m - first) * chunks_per_tok;
+  if (e < total) {
+    const int i = first + (int)(e / chunks_per_tok);
+    const int r = (int)(e % chunks_per_tok);
+    const size_t src = ((size_t)b * n_new + i) * (size_t)(g.H * g.D) + (size_t)r * 8;
+    const int slot = (int)((old + i) % g.tail);
+    const size_t dst = ((size_t)b * g.tail + slot) * (size_t)(g.H * g.D) + (size_t)r * 8;
+    *reinterpret_cast<uint4*>(d.tail_k + dst) = *reinterpret_cast<const uint4*>(k_new + src);
+    *reinterpret_cast<uint4*>(d.tail_v + dst) = *reinterpret_cast<const uint4*>(v_new + src);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && d.own_pool) d.own_qgroups[b] = (int)(nw / kGroup);
+}
+
+}  // namespace
+
+hipError_t launch_append(const Geom& g, const CellDesc* desc_dev, const CellDesc& dh,
+                         const uint16_t* k_new, const uint16_t* v_new, int batch, int n_new,
+                         const int32_t* n_new_dev, const int32_t* seq_lens,
+                         const int32_t* page_table, int pt_stride, hipStream_t stream) {
+  if (dh.own_pool) {
+    const dim3 grid((unsigned)((n_new + kGroup - 1) / kGroup + 1), (unsigned)g.H, (unsigned)batch);
+    if (dh.own_bits == 4)
+      quantize_group_kernel<4><<<grid, 128, 0, stream>>>(g, desc_dev, k_new, v_new, n_new, n_new_dev,
+                                                         seq_lens, page_table, pt_stride);
+    else
+      quantize_group_kernel<2><<<grid, 128, 0, stream>>>(g, desc_dev, k_new, v_new, n_new, n_new_dev,
+                                                         seq_lens, page_table, pt_stride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // The ring kernel must follow the quantize kernel: that one reads ring slots this one
+  // may overwrite. Both are on `stream`, so they run in order.
+  const int first = n_new > g.tail ? n_new - g.tail : 0;
+  const int64_t chunks = (int64_t)(n_new - first) * (g.H * g.D / 8);
+  const dim3 grid2((unsigned)((chunks + 255) / 256), (unsigned)batch);
+  tail_write_kernel<<<grid2, 256, 0, stream>>>(g, desc_dev, k_new, v_new, n_new, n_new_dev,
+                                               seq_lens, pt_stride);
+  return hipGetLastError();
+}
+
+}  // namespace loopkv

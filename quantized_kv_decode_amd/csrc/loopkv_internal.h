@@ -1,0 +1,112 @@
+// Internal definitions shared by the host side of libloopkv and its HIP kernels.
+//
+// Page layout (what a page holds follows "Loop-Aware KV Cache Compression for Serving
+// Looped Transformers", section 3.3 "Bit-plane V layout" and section 3.4 "Layout"; the byte
+// order below is this library's choice). A page is H head blocks, head-major. One head
+// block of a page of P tokens, D channels and NVG value groups:
+//
+//   KSZ  4*D          fp16 (scale, zero) per channel of the key group starting in this page
+//   KC   P*D*bits/8   key codes, 32-bit words W[cb][t] at word cb*P + t
+//                       INT4: channel 8*cb + i in bits 4i..4i+3
+//                       INT2: channel 16*cb + i in bits 2i..2i+1
+//   VC   P*D/4        INT4 high plane / INT2 codes, W[cb][t] at word cb*P + t,
+//                       channel 16*cb + i in bits 2i..2i+1
+//   VSZ  4*P*NVG      fp16 (scale, zero) per (token, value group), token-major
+//   VLO  P*D/4        INT4 low plane, token-major W[t][cb] at word t*(D/16) + cb, so one
+//                       token's low plane is D/4 contiguous bytes
+//
+// Column-major code words give each lane of a wave contiguous 16-byte loads of several
+// tokens of the same channels; the token-major low plane makes a hot token's fetch one
+// contiguous D/4-byte row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "loopkv.h"
+
+namespace loopkv {
+
+constexpr int kGroup = 32;     // tokens per key quantization group
+constexpr int kHeadDim = 128;  // the only head_dim this build implements
+
+enum DeviceError : uint32_t {
+  kErrLength = 1u,  // a sequence length outside [0, max context]
+  kErrPage = 2u,    // a page id outside [0, num_pages)
+  kErrTail = 4u,    // more unquantized tokens than the ring holds
+};
+
+struct Layout {
+  int32_t ksz, kc, vc, vsz, vlo, total;
+};
+
+__host__ __device__ inline Layout head_layout(int bits, int page_tokens, int head_dim, int nvg) {
+  Layout l;
+  l.ksz = 0;
+  l.kc = 4 * head_dim;
+  l.vc = l.kc + page_tokens * head_dim * bits / 8;
+  l.vsz = l.vc + page_tokens * head_dim / 4;
+  l.vlo = l.vsz + 4 * page_tokens * nvg;
+  l.total = l.vlo + (bits == 4 ? page_tokens * head_dim / 4 : 0);
+  return l;
+}
+
+// One descriptor per cell, built by loopkv_plan_load and kept in the arena.
+struct CellDesc {
+  uint8_t* read_pool;         // pool read by decode: own, or the final loop's (REUSE)
+  uint8_t* own_pool;          // pool written by append; null for REUSE
+  uint16_t* tail_k;           // bf16 ring [max_batch][tail_tokens][H][D]
+  uint16_t* tail_v;
+  int32_t* src_qgroups;       // quantized-group counters of the cell whose pool is read
+  int32_t* own_qgroups;       // this cell's counters (written by append for own storage)
+  int64_t read_page_bytes;
+  int64_t own_page_bytes;
+  int32_t read_bits;          // 2 or 4
+  int32_t own_bits;           // 0 (REUSE), 2 or 4
+  int32_t gated;              // read_bits == 4
+  int32_t code;
+};
+
+// Static shape, passed by value to every kernel.
+struct Geom {
+  int32_t H;             // kv heads (= q heads)
+  int32_t D;             // head dim
+  int32_t P;             // page tokens
+  int32_t nvg;           // value groups per head
+  int32_t v_group;       // channels per value group
+  int32_t tail;          // ring tokens
+  int32_t max_ctx;       // max_pages_per_seq * P
+  int32_t max_splits;
+  int64_t num_pages;
+  uint32_t* err;         // device error word
+};
+
+// Launchers implemented next to their kernels.
+hipError_t launch_append(const Geom& g, const CellDesc* desc_dev, const CellDesc& desc_host,
+                         const uint16_t* k_new, const uint16_t* v_new, int batch, int n_new,
+                         const int32_t* n_new_dev, const int32_t* seq_lens,
+                         const int32_t* page_table, int pt_stride, hipStream_t stream);
+
+struct DecodeCall {
+  const CellDesc* desc_dev;
+  const uint16_t* q;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int32_t pt_stride;
+  int32_t batch;
+  float tau;
+  float sm_scale;
+  int32_t split_tokens;   // 0 = one split
+  int32_t n_split;
+  const float* seed;
+  uint8_t* mask;
+  int32_t mask_stride;
+  unsigned long long* stats;
+  float* out;
+  float* partials;        // [batch, H, max_splits, D + 2]
+};
+
+hipError_t launch_decode(const Geom& g, const CellDesc& desc_host, const DecodeCall& c,
+                         hipStream_t stream);
+
+}  // namespace loopkv
