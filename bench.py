@@ -1,0 +1,284 @@
+"""Benchmark: one LoopKV decode step (every cell's fused decode-attention launch, in model order)
+on one MI355X, on a synthetic Ouro-1.4B-shaped cache.
+
+Default workload: 24 layers x 4 loops = 96 cells, 16 KV heads x 128, batch 64, context 8192,
+seeded plan of 40% INT4 / 35% INT2 / 25% reuse-the-final-loop, tau = 0.01, one split per row.
+A step is the 96 decode launches back to back on one stream; inputs are resident in HBM.
+
+Prints one JSON line: value = microseconds per decode step (lower is better), plus the achieved
+algorithmic HBM bandwidth of the decode kernel against MI355X's 8 TB/s (`roofline`) and the
+fp64 CPU oracle timed on a bounded sample on this host (`cpu_baseline`).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+# Algorithmic bytes per (token, head) read by decode, 128-channel value groups.
+INT4_BASE, INT4_LO, INT2_BYTES = 116.0, 32.0, 84.0
+
+WORKLOADS = {
+    # name: (layers, loops, batch, context, p_int4, p_reuse, split_tokens, heavy_tail)
+    "ouro1.4b-96cells-b64-ctx8k": (24, 4, 64, 8192, 0.40, 0.25, 0, False),
+    "ouro2.6b-192cells-b16-ctx32k": (48, 4, 16, 32768, 0.30, 0.25, 8192, True),
+    "one-layer-4loops-b8-ctx4k": (1, 4, 8, 4096, None, None, 1024, False),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in ["decode.hip", "loopkv_internal.h"]:
+        h.update(open(os.path.join(ROOT, "quantized_kv_decode_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def build_cache(name, seed, tau):
+    import torch
+    from quantized_kv_decode_amd import loopkv as L
+    from quantized_kv_decode_amd import synth
+    from quantized_kv_decode_amd.cache import LoopKVCache
+
+    layers, loops, B, N, p4, pr, split, heavy = WORKLOADS[name]
+    if p4 is None:
+        plan = np.array([[4], [4], [2], [4]], np.uint8)
+    else:
+        plan = synth.plan(layers, loops, seed, p4, pr)
+    P = 32
+    pages_per_seq = N // P
+    shape = L.make_shape(num_layers=layers, num_loops=loops, page_tokens=P, v_group=128, max_batch=B,
+                         max_pages_per_seq=pages_per_seq, tail_tokens=64,
+                         max_splits=max(1, N // split) if split else 1, num_pages=B * pages_per_seq)
+    cache = LoopKVCache(shape, plan)
+    pt_np, _ = synth.page_table([N] * B, P, seed + 1, shuffle=True)
+    pt = torch.as_tensor(pt_np).cuda()
+    zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
+    t0 = time.time()
+    for t in range(loops):
+        for l in range(layers):
+            if plan[t, l] == L.REUSE:
+                continue
+            cs = seed * 100003 + t * 1000 + l
+            k = synth.keys(B, N, 16, 128, cs, device="cuda", heavy_tail=heavy)
+            v = synth.values(B, N, 16, 128, cs, device="cuda")
+            cache.append(l, t, k, v, zeros, pt)
+            del k, v
+    torch.cuda.synchronize()
+    log(f"[bench] filled {int((plan != 0).sum())} own cells in {time.time() - t0:.1f}s; "
+        f"arena {cache.bytes.arena_bytes / 2**30:.1f} GiB")
+    return cache, plan, pt, pt_np, dict(layers=layers, loops=loops, B=B, N=N, split=split, heavy=heavy)
+
+
+def run_step(cache, plan, qs, outs, seq, pt, tau, split, stats=None):
+    loops, layers = plan.shape
+    i = 0
+    for t in range(loops):
+        for l in range(layers):
+            cache.decode(l, t, qs[i], seq, pt, tau=tau, split_tokens=split, out=outs[i],
+                         stats=None if stats is None else stats[i])
+            i += 1
+
+
+def algorithmic_bytes(plan, hot_frac, B, N, H=16, n_split=1):
+    """Bytes one decode step reads/writes by the path's definition: per history (token, head)
+    116 + 32*h bytes for an INT4-read cell and 84 for an INT2-read cell, plus q, out, the
+    page table, and split partials."""
+    loops, layers = plan.shape
+    total = 0.0
+    per_cell = []
+    i = 0
+    for t in range(loops):
+        for l in range(layers):
+            src = plan[loops - 1, l] if plan[t, l] == 0 else plan[t, l]
+            per_tok = INT4_BASE + INT4_LO * hot_frac[i] if src == 4 else INT2_BYTES
+            b = B * N * H * per_tok + B * H * 128 * (2 + 4) + B * (N // 32) * 4
+            if n_split > 1:
+                b += 2 * B * H * n_split * 130 * 4
+            per_cell.append(b)
+            total += b
+            i += 1
+    return total, per_cell
+
+
+def cpu_baseline(cfg, plan, tau, seed, budget_s=15.0):
+    """The fp64 oracle on a bounded sample: for a few cells (INT4, INT2, reuse) and requests, the
+    oracle packs its own quantization of the same synthetic K/V into pages (untimed), then the
+    timed part reads the packed rows back, dequantizes, builds the fetch mask and runs fp64
+    attention. Extrapolated linearly in (token, head) rows to the whole step."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    from quantized_kv_decode_amd import synth
+
+    layers, loops, B, N = cfg["layers"], cfg["loops"], cfg["B"], cfg["N"]
+    H = 16
+    cells = []
+    for code in (4, 2, 0):
+        idx = np.argwhere(plan == code)
+        if len(idx):
+            cells.append(tuple(int(x) for x in idx[0]))
+    rows_done = 0
+    timed = 0.0
+    reqs = [0]
+    with threadpool_limits(limits=1):
+        for (t, l) in cells:
+            st, sl = (loops - 1, l) if plan[t, l] == 0 else (t, l)
+            bits = int(plan[st, sl])
+            cs = seed * 100003 + st * 1000 + sl
+            # the same generator as the GPU fill, then the sampled request copied to the host
+            k = synth.keys(B, N, H, 128, cs, device="cuda", heavy_tail=cfg["heavy"])[reqs].double().cpu().numpy()
+            v = synth.values(B, N, H, 128, cs, device="cuda")[reqs].double().cpu().numpy()
+            q = synth.queries(B, H, 128, 777 + t * 100 + l, device="cuda")[reqs].double().cpu().numpy()
+            for bi in range(len(reqs)):
+                heads = [O.quantize_head(k[bi, :, h], v[bi, :, h], bits, 128) for h in range(H)]
+                pt = np.arange(N // 32)[None, :]
+                pool = O.pack_pool(bits, 32, [heads], pt, N // 32)
+                for h in range(H):
+                    t0 = time.perf_counter()
+                    qh = O.unpack_pool_head(bits, 32, pool, pt[0], N, h, H)
+                    O.decode_head(q[bi, h], qh, np.zeros((0, 128)), np.zeros((0, 128)),
+                                  sm_scale=1 / math.sqrt(128), tau=tau, split_tokens=cfg["split"])
+                    timed += time.perf_counter() - t0
+                    rows_done += 1
+                    if timed > budget_s:
+                        break
+                if timed > budget_s:
+                    break
+    rows_step = loops * layers * B * H
+    per_row = timed / rows_done
+    us_step = per_row * rows_step * 1e6
+    return {"value": us_step, "unit": "us/step", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} (request, head) rows of {len(cells)} cells (INT4 / INT2 / reuse), "
+                      f"{N} tokens each, {timed:.1f} s timed; extrapolated x{rows_step / rows_done:.0f} "
+                      f"to {rows_step} rows per step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ouro1.4b-96cells-b64-ctx8k", choices=sorted(WORKLOADS))
+    ap.add_argument("--tau", type=float, default=0.01)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for {args.gpus}). "
+              "See DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_kv_decode_amd import synth
+
+    torch.cuda.set_device(0)
+    cache, plan, pt, pt_np, cfg = build_cache(args.workload, args.seed, args.tau)
+    loops, layers = plan.shape
+    B, N, split = cfg["B"], cfg["N"], cfg["split"]
+    ncell = loops * layers
+    qs = [synth.queries(B, 16, 128, 777 + t * 100 + l, device="cuda") for t in range(loops) for l in range(layers)]
+    outs = [torch.empty(B, 16, 128, dtype=torch.float32, device="cuda") for _ in range(ncell)]
+    seq = torch.full((B,), N, dtype=torch.int32, device="cuda")
+
+    # Hot fractions (one pass with device counters, untimed).
+    stats = torch.zeros(ncell, 4, dtype=torch.int64, device="cuda")
+    run_step(cache, plan, qs, outs, seq, pt, args.tau, split, stats=[stats[i] for i in range(ncell)])
+    torch.cuda.synchronize()
+    st = stats.cpu().numpy().astype(np.float64)
+    hot_frac = np.where(st[:, 2] > 0, st[:, 1] / np.maximum(st[:, 2], 1), 0.0)
+    gated = st[:, 2] > 0
+    overall_hot = float(st[gated, 1].sum() / max(st[gated, 2].sum(), 1)) if gated.any() else 0.0
+    assert cache.device_errors() == 0
+
+    if args.calibrate_copy:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        run_step(cache, plan, qs, outs, seq, pt, args.tau, split)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record(stream)
+    for i in range(args.steps):
+        run_step(cache, plan, qs, outs, seq, pt, args.tau, split)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    total_ms = ev[0].elapsed_time(ev[-1])
+    med_ms = float(np.median(step_ms))
+    for o in outs:
+        assert torch.isfinite(o).all()
+
+    n_split = (N + split - 1) // split if split else 1
+    alg_bytes, _ = algorithmic_bytes(plan, hot_frac, B, N, n_split=n_split)
+    per_launch_bytes = alg_bytes / ncell
+    per_launch_s = med_ms / 1e3 / ncell
+    achieved = per_launch_bytes / per_launch_s / 1e9
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if os.path.exists(tfile):
+        tj = json.load(open(tfile))
+        if tj.get("kernel_hash") == kernel_hash() and tj.get("workload") == args.workload:
+            traffic = tj.get("hbm_bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, plan, args.tau, args.seed, args.cpu_budget)
+
+    line = {
+        "metric": "fused LoopKV decode attn: µs/step and achieved HBM TB/s vs peak, 1 MI355X",
+        "value": round(med_ms * 1e3, 1),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(med_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8 codes, fp16 scales, f32 math",
+        "data": "synthetic (seeded Gaussian K/V/q, 4 outlier key channels x10 per cell and head)",
+        "config": {"workload": args.workload, "layers": layers, "loops": loops, "cells": ncell,
+                   "kv_heads": 16, "head_dim": 128, "batch": B, "context": N, "tau": args.tau,
+                   "split_tokens": split, "plan_counts": {"int4": int((plan == 4).sum()),
+                                                          "int2": int((plan == 2).sum()),
+                                                          "reuse": int((plan == 0).sum())},
+                   "page_tokens": 32, "v_group": 128, "plan_seed": args.seed},
+        "achieved_TBps": round(alg_bytes / (med_ms / 1e3) / 1e12, 3),
+        "hot_fraction": round(overall_hot, 4),
+        "alg_bytes_per_step": int(alg_bytes),
+        "mean_ms_per_step": round(total_ms / args.steps, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "kernel_hash": kernel_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
