@@ -13,23 +13,26 @@
 //  - split partials merge by log-sum-exp, which gives the exact softmax (section 3.4).
 //
 // Work mapping (CDNA4, wave64): one workgroup of NW waves per (request, head, split). In each
-// round every wave takes one 32-token group; the group maxima are combined across the waves
-// through LDS as a prefix maximum, so the hot/cold decisions are exactly those of streaming the
-// split group by group, whatever NW is. Each wave keeps its own online-softmax state; the waves
-// merge at the end. NW is chosen so that every workgroup of a launch is resident at once.
+// round every wave takes two consecutive 32-token groups, lanes 0..31 the first and lanes
+// 32..63 the second. The group maxima are combined across the waves through LDS as a prefix
+// maximum, so the hot/cold decisions are exactly those of streaming the split group by group.
+// Each wave keeps its own online-softmax state; the waves merge at the end.
 //
-// Latency hiding: every data-independent load of a wave's next group (key codes and scales,
-// value high plane or INT2 codes, value scales) is issued one round ahead into a second set of
-// registers (the round loop alternates the two sets); the low planes of a round's hot tokens
-// are loaded in that round and accumulated in the next. Pool and tail pointers are global and
-// page-table / descriptor reads constant address space, so the loads are global (not flat)
-// and uniform indices become scalar loads.
+// Latency hiding: every data-independent load of a wave's next two groups (key codes and
+// scales, value high plane or INT2 codes, value scales) is issued one round ahead into a second
+// set of registers (the round loop alternates the two sets); the low planes of a round's hot
+// tokens are loaded in that round and accumulated in the next.
 //
-// Code unpacking: a 2- or 4-bit code placed in the low bits of an fp8 (E4M3) byte converts
-// exactly to code * u, with u the value of byte 0x01, because E4M3's subnormals and first
-// binade are evenly spaced up to 15 * u. One masked word thus yields four codes as floats with
-// two packed conversions; the constant u (and the factor 4 of codes sitting two bits up in
-// their byte) folds into the query or into the per-channel output scale.
+// Arithmetic:
+//  - keys: a 2- or 4-bit code in the low bits of an fp8 (E4M3) byte converts exactly to
+//    code * u (u = the value of byte 0x01), since E4M3's subnormals and first binade are evenly
+//    spaced up to 15u; one masked word gives four codes as floats in two packed conversions.
+//    The score is an fp32 FMA chain, so the hot/cold test sees fp32-accurate scores.
+//  - values (INT4 high plane, INT2 codes): two tokens' words are interleaved with one byte
+//    permute so each 16-bit half holds one token's channels; a code moved to mantissa bits 6..9
+//    and OR-ed with the exponent of 1.0 is the fp16 number 1 + c/16 or 1 + c/4, and one
+//    v_dot2_f32_f16 accumulates both tokens' weighted codes in fp32. The constant offset
+//    (the sum of the fp16 weights) is removed once at the end.
 #include "loopkv_internal.h"
 
 #define LKV_GLOBAL __attribute__((address_space(1)))
@@ -39,8 +42,10 @@ namespace loopkv {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kWScale = 256.f;        // fp16 value weights are scaled up to stay normal
 
 typedef float float2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef const LKV_GLOBAL uint8_t* gbytes;
 
@@ -71,6 +76,13 @@ template <bool HI>
 __device__ __forceinline__ float2v cvt2(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
 }
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ half2v pack_h2(float a, float b) {
+  return __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+__device__ __forceinline__ float dot2(half2v a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(a, __builtin_bit_cast(half2v, b), c, false);
+}
 
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -78,8 +90,9 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Maximum over lanes 0..31 (the values of lanes 32..63 duplicate them), broadcast to all.
-__device__ __forceinline__ float max32(float v) {
+__device__ __forceinline__ float dpp_max(float v, int ctrl_dummy);
+// Maximum within each 16-lane row, broadcast to the row.
+__device__ __forceinline__ float row_max16(float v) {
   v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                    0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));   // quad xor 1
   v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
@@ -88,9 +101,10 @@ __device__ __forceinline__ float max32(float v) {
                    0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));  // half-row mirror
   v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                    0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));  // row mirror
-  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  return fmaxf(a, b);
+  return v;
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -103,8 +117,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// 16 two-bit codes of a word (channel i at bits 2i) as floats in "scaled units": channel i is
-// returned as code * u * (i odd ? 4 : 1).
+// 16 two-bit codes of a word (channel i at bits 2i) as floats: code * u * (i odd ? 4 : 1).
 __device__ __forceinline__ void unpack16(uint32_t w, float (&x)[16]) {
   const uint32_t m0 = w & 0x03030303u, m1 = w & 0x0C0C0C0Cu;
   const uint32_t w4 = w >> 4;
@@ -128,26 +141,59 @@ __device__ __forceinline__ void unpack8(uint32_t w, float (&x)[8]) {
   x[1] = c.x; x[3] = c.y; x[5] = d.x; x[7] = d.y;
 }
 
+// (x & m) | o in one VALU op. VOP3 takes no literal constant and at most one SGPR on gfx950,
+// so the mask is held in a VGPR and the OR constant in an SGPR (Masks below).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "s"(o));
+  return r;
+}
+struct Masks {
+  uint32_t one, m89, m67;   // fp16 1.0 in both halves; code bits 8..9 / 6..7 of both halves
+};
+
+// acc[c] += w0 * code(t0, c) + w1 * code(t1, c) for the 16 channels of two tokens' 2-bit code
+// words, in offset units: each code enters as the fp16 number 1 + code/4 (even channels) or
+// 1 + code/16 (odd channels).
+__device__ __forceinline__ void dot2_pair(uint32_t w0, uint32_t w1, half2v wp, const Masks& mk,
+                                          float (&acc)[16]) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    // channels 8*half .. 8*half+7 of token t0 in bits 0..15, of token t1 in bits 16..31
+    const uint32_t s = __builtin_amdgcn_perm(w1, w0, half ? 0x07060302u : 0x05040100u);
+    const uint32_t l4 = s << 4, l8 = s << 8, r4 = s >> 4, r8 = s >> 8;
+    float* a = acc + 8 * half;
+    a[0] = dot2(wp, and_or(l8, mk.m89, mk.one), a[0]);
+    a[1] = dot2(wp, and_or(l4, mk.m67, mk.one), a[1]);
+    a[2] = dot2(wp, and_or(l4, mk.m89, mk.one), a[2]);
+    a[3] = dot2(wp, and_or(s, mk.m67, mk.one), a[3]);
+    a[4] = dot2(wp, and_or(s, mk.m89, mk.one), a[4]);
+    a[5] = dot2(wp, and_or(r4, mk.m67, mk.one), a[5]);
+    a[6] = dot2(wp, and_or(r4, mk.m89, mk.one), a[6]);
+    a[7] = dot2(wp, and_or(r8, mk.m67, mk.one), a[7]);
+  }
+}
+
 template <int NVG, int NW>
 struct Smem {
   alignas(16) float q[kHeadDim];
-  alignas(16) float red[NW][16][36];    // per-wave key partials [channel block][token]
-  alignas(16) float wbuf[NW][NVG][32];  // per-wave value weights [value group][token]
-  int hot_list[NW][32];
-  float gmax[2][NW];
+  alignas(16) float red[NW][2][16][36];   // per-wave key partials [half][channel block][token]
+  alignas(16) float wbuf[NW][NVG][64];    // per-wave value weights [value group][token of pair]
+  int hot_list[NW][64];
+  float gmax[2][NW][2];
   float fin_acc[NW][kHeadDim];
   float fin_M[NW], fin_L[NW], fin_C[NW][NVG];
   unsigned long long cnt_hot;
 };
 
-// Per-lane registers of one group, loaded one round ahead.
+// Per-lane registers of one pair of groups, loaded one round ahead.
 template <int BITS, int NVG>
-struct GroupRegs {
-  static constexpr int KCW = BITS == 4 ? 2 : 1;   // 16-byte loads of key code words
+struct PairRegs {
+  static constexpr int KCW = BITS == 4 ? 4 : 2;   // 16-byte loads of key code words
   static constexpr int KSW = BITS == 4 ? 2 : 4;   // 16-byte loads of key (s, z) words
   u32x4 kc[KCW];
   u32x4 ksz[KSW];
-  u32x4 vc;
+  u32x4 vc[2];
   uint32_t vsz[NVG];
 };
 
@@ -169,37 +215,60 @@ __device__ __forceinline__ gbytes page_block(const RowCtx& r, int logical_page) 
   return r.pool + (int64_t)pid * r.page_bytes + r.head_off;
 }
 
+// Page blocks of a pair of groups: [group of the pair][page within the group].
+template <int P>
+struct PairPages {
+  gbytes b[2][2];
+  __device__ __forceinline__ gbytes lane_block(int half, int t) const {
+    gbytes g0 = half ? b[1][0] : b[0][0];
+    if (P == kGroup) return g0;
+    gbytes g1 = half ? b[1][1] : b[0][1];
+    return t < P ? g0 : g1;
+  }
+};
+
+template <int P>
+__device__ __forceinline__ PairPages<P> pair_pages(const RowCtx& r, int gA, int gB) {
+  PairPages<P> pp;
+  constexpr int PPG = kGroup / P;   // pages per group
+  pp.b[0][0] = page_block(r, gA * PPG);
+  pp.b[1][0] = page_block(r, gB * PPG);
+  if (PPG == 2) {
+    pp.b[0][1] = page_block(r, gA * PPG + 1);
+    pp.b[1][1] = page_block(r, gB * PPG + 1);
+  } else {
+    pp.b[0][1] = pp.b[0][0];
+    pp.b[1][1] = pp.b[1][0];
+  }
+  return pp;
+}
+
 template <int BITS, int NVG, int P>
-__device__ __forceinline__ void load_group(GroupRegs<BITS, NVG>& g, const RowCtx& r, const Layout& lay,
-                                           int grp, int lane) {
+__device__ __forceinline__ void load_pair(PairRegs<BITS, NVG>& g, const PairPages<P>& pp,
+                                          const Layout& lay, int lane) {
   constexpr int KCH = 32 / BITS;
   constexpr int NCB = kHeadDim / KCH;
-  constexpr int KTOK = kGroup * NCB / 64;
-  const int cb = lane % NCB, tq = lane / NCB;
-  const int t0 = tq * KTOK;
-  const int lp0 = grp * (kGroup / P);
-  gbytes blk0 = page_block(r, lp0);
-  gbytes blk1 = P == kGroup ? blk0 : page_block(r, lp0 + 1);
+  constexpr int KTOK = NCB;                 // tokens per lane in a 32-lane half
+  const int half = lane >> 5, hl = lane & 31;
+  const int cb = hl % NCB, t0 = (hl / NCB) * KTOK;
   {  // key codes of KTOK tokens of channel block cb
-    gbytes bb = t0 < P ? blk0 : blk1;
-    const LKV_GLOBAL u32x4* p = gp<u32x4>(bb + lay.kc + 4 * (cb * P + t0 % P));
+    const LKV_GLOBAL u32x4* p = gp<u32x4>(pp.lane_block(half, t0) + lay.kc + 4 * (cb * P + t0 % P));
 #pragma unroll
-    for (int i = 0; i < GroupRegs<BITS, NVG>::KCW; ++i) g.kc[i] = p[i];
+    for (int i = 0; i < PairRegs<BITS, NVG>::KCW; ++i) g.kc[i] = p[i];
   }
   {  // key (s, z) of the lane's channels, stored with the group's first page
-    const LKV_GLOBAL u32x4* p = gp<u32x4>(blk0 + lay.ksz + 4 * cb * KCH);
+    const LKV_GLOBAL u32x4* p = gp<u32x4>(pp.lane_block(half, 0) + lay.ksz + 4 * cb * KCH);
 #pragma unroll
-    for (int i = 0; i < GroupRegs<BITS, NVG>::KSW; ++i) g.ksz[i] = p[i];
+    for (int i = 0; i < PairRegs<BITS, NVG>::KSW; ++i) g.ksz[i] = p[i];
   }
-  {  // value codes / high plane: 16 channels x 4 tokens
-    const int cbv = lane & 7, t4 = (lane >> 3) * 4;
-    gbytes bb = t4 < P ? blk0 : blk1;
-    g.vc = *gp<u32x4>(bb + lay.vc + 4 * (cbv * P + t4 % P));
+  {  // value codes / high plane: 16 channels x 8 tokens
+    const int cbv = hl & 7, tv = (hl >> 3) * 8;
+    const LKV_GLOBAL u32x4* p = gp<u32x4>(pp.lane_block(half, tv) + lay.vc + 4 * (cbv * P + tv % P));
+    g.vc[0] = p[0];
+    g.vc[1] = p[1];
   }
-  {  // value (s, z) of token `lane` (lanes 0..31)
-    const int t = lane & 31;
-    gbytes bb = t < P ? blk0 : blk1;
-    const LKV_GLOBAL uint32_t* p = gp<uint32_t>(bb + lay.vsz) + (t % P) * NVG;
+  {  // value (s, z) of token hl
+    const LKV_GLOBAL uint32_t* p = gp<uint32_t>(pp.lane_block(half, hl) + lay.vsz) + (hl % P) * NVG;
 #pragma unroll
     for (int i = 0; i < NVG; ++i) g.vsz[i] = p[i];
   }
@@ -208,39 +277,66 @@ __device__ __forceinline__ void load_group(GroupRegs<BITS, NVG>& g, const RowCtx
 // Softmax and value accumulation state of one wave.
 template <int NVG>
 struct WaveState {
-  float M, Lsum, m_run;
+  float M, Lsum, m_run, W;       // W: sum of the fp16 value weights (offset of acc)
   float Csum[NVG];
-  float acc[16];                 // scaled units, channels 16*cbv + i
+  // Value accumulator of channels 16*cbv + i in offset units: the high plane / INT2 codes enter
+  // through dot2 as w' * (1 + code * f_i) with w' = kWScale * weight, f_i = 1/4 (even i) or 1/16
+  // (odd i), and W collects the w'; low planes and exact tail values are added without the
+  // offset. True weighted sum of channel i = (acc[i] - W) / (f_i * kWScale).
+  float acc[16];
   uint32_t lo_word[4];           // low planes loaded last round
-  float lo_wt[4];                // their weights (0: nothing loaded)
+  float lo_wt[4];                // their odd-channel weights (0: nothing loaded)
   unsigned long long hot;
 };
 
 struct RoundConst {
-  float scale2, log2tau, u;
+  float scale2, log2tau, u, lo_scale;   // lo_scale = 1 / (kWScale * u)
   bool gated;
   int w, lane, gs, ge;
   uint8_t* mask_row;
+  Masks mk;
 };
+
+// Adds a low-plane word (16 channels, 2-bit codes) with odd-channel weight wo: a low code is a
+// quarter of a value code step, and unpack16's scale (u, and 4u on odd channels) and the offset
+// units (f = 1/4 even, 1/16 odd) fold into wo and 16 * wo.
+__device__ __forceinline__ void add_lo(uint32_t word, float wo, float (&acc)[16]) {
+  float x[16];
+  unpack16(word, x);
+  const float we = 16.f * wo;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    acc[i] = fmaf(we, x[i], acc[i]);
+    acc[i + 1] = fmaf(wo, x[i + 1], acc[i + 1]);
+  }
+}
 
 template <int BITS, int NVG, int P, int NW>
 __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st,
-                                           const GroupRegs<BITS, NVG>& cur, GroupRegs<BITS, NVG>& nxt,
+                                           const PairRegs<BITS, NVG>& cur, PairRegs<BITS, NVG>& nxt,
                                            const RowCtx& r, const Layout& lay, const RoundConst& k,
                                            const float (&qv)[32 / BITS], int rd) {
   constexpr int KCH = 32 / BITS;
   constexpr int NCB = kHeadDim / KCH;
-  constexpr int KTOK = kGroup * NCB / 64;
+  constexpr int KTOK = NCB;
   const int w = k.w, lane = k.lane;
-  const int cb = lane % NCB, tq = lane / NCB;
-  const int cbv = lane & 7, tq8 = lane >> 3;
+  const int half = lane >> 5, hl = lane & 31;
+  const int cb = hl % NCB, t0 = (hl / NCB) * KTOK;
+  const int cbv = lane & 7;
   const int vg_lane = (cbv * 16) / (kHeadDim / NVG);
-  const int grp = k.gs + rd * NW + w;
-  const bool active = grp < k.ge;
-  const int nxt_grp = grp + NW;
-  if (nxt_grp < k.ge) load_group<BITS, NVG, P>(nxt, r, lay, nxt_grp, lane);
+  const int gA = k.gs + rd * 2 * NW + 2 * w;
+  const bool active = gA < k.ge;
+  const bool validB = gA + 1 < k.ge;
+  const bool my_valid = half ? validB : active;
+  {
+    const int nA = gA + 2 * NW;
+    if (nA < k.ge) {
+      const int nB = nA + 1 < k.ge ? nA + 1 : nA;   // never index past the history
+      load_pair<BITS, NVG, P>(nxt, pair_pages<P>(r, nA, nB), lay, lane);
+    }
+  }
 
-  // ---- scores of the group (key codes read first, section 3.3)
+  // ---- scores of both groups (key codes read first, section 3.3)
   float s2 = -INFINITY;
   if (active) {
     float qs[KCH], ke = 0.f, ko = 0.f;
@@ -248,7 +344,7 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const uint32_t sz = kszw[i];
-      qs[i] = qv[i] * f16_lo(sz);
+      qs[i] = fmaf(qv[i], f16_lo(sz), 0.f);      // fp16 operand: one v_fma_mix_f32
       if (BITS == 2 && (i & 1)) ko = fmaf(qv[i], f16_hi(sz), ko);
       else ke = fmaf(qv[i], f16_hi(sz), ke);
     }
@@ -272,37 +368,46 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
       }
       part[j] = a;
     }
-    float* red = &sm.red[w][cb][tq * KTOK];
+    float* red = &sm.red[w][half][cb][t0];
 #pragma unroll
     for (int j = 0; j < KTOK; j += 4)
       *reinterpret_cast<float4*>(red + j) = make_float4(part[j], part[j + 1], part[j + 2], part[j + 3]);
     wave_lds_sync();
-    // all 64 lanes: lane l sums half of the channel blocks of token l & 31
-    const int t = lane & 31, half = lane >> 5;
     float raw = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < NCB / 2; ++kk) raw += sm.red[w][half * (NCB / 2) + kk][t];
-    raw += __shfl_xor(raw, 32);
-    s2 = raw * k.scale2;
+    for (int kk = 0; kk < NCB; ++kk) raw += sm.red[w][half][kk][hl];
+    s2 = my_valid ? raw * k.scale2 : -INFINITY;
   }
-  const float gmax_w = active ? max32(s2) : -INFINITY;
-  if (lane == 0) sm.gmax[rd & 1][w] = gmax_w;
+  float gmA = -INFINITY, gmB = -INFINITY;
+  if (active) {
+    const float rm = row_max16(s2);
+    gmA = fmaxf(lane_f(rm, 0), lane_f(rm, 16));
+    gmB = fmaxf(lane_f(rm, 32), lane_f(rm, 48));
+  }
+  if (lane == 0) {
+    sm.gmax[rd & 1][w][0] = gmA;
+    sm.gmax[rd & 1][w][1] = gmB;
+  }
   __syncthreads();
-  float mpre = st.m_run, mall = st.m_run;
+  float mpreA = st.m_run, mall = st.m_run;
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    const float x = sm.gmax[rd & 1][i];
-    if (i <= w) mpre = fmaxf(mpre, x);
-    mall = fmaxf(mall, x);
+    const float x0 = sm.gmax[rd & 1][i][0], x1 = sm.gmax[rd & 1][i][1];
+    if (i <= w) mpreA = fmaxf(mpreA, x0);
+    if (i < w) mpreA = fmaxf(mpreA, x1);
+    mall = fmaxf(mall, fmaxf(x0, x1));
   }
+  const float mpreB = fmaxf(mpreA, gmB);
   st.m_run = mall;
   if (!active) return;
 
   // ---- online softmax: rescale only when the wave's maximum grows
-  if (gmax_w > st.M) {
+  const float gm = fmaxf(gmA, gmB);
+  if (gm > st.M) {
     if (st.M != -INFINITY) {
-      const float f = exp2f(st.M - gmax_w);
+      const float f = fexp2(st.M - gm);
       st.Lsum *= f;
+      st.W *= f;
 #pragma unroll
       for (int i = 0; i < NVG; ++i) st.Csum[i] *= f;
 #pragma unroll
@@ -310,74 +415,86 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.lo_wt[i] *= f;
     }
-    st.M = gmax_w;
+    st.M = gm;
   }
   // ---- last round's low planes
   if (BITS == 4) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (st.lo_wt[kk] != 0.f) {
-        float x[16];
-        unpack16(st.lo_word[kk], x);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st.acc[i] = fmaf(st.lo_wt[kk], x[i], st.acc[i]);
-      }
-    }
+    for (int kk = 0; kk < 4; ++kk)
+      if (st.lo_wt[kk] != 0.f) add_lo(st.lo_word[kk], st.lo_wt[kk], st.acc);
   }
 
-  // ---- per token (lanes 0..31): weight, hot/cold, value scale/zero folds
-  bool hot = true;
-  if (lane < kGroup) {
-    const float p = exp2f(s2 - st.M);
-    if (k.gated) hot = !((s2 - mpre) < k.log2tau);
+  // ---- per token (every lane): weight, hot/cold, value scale/zero folds
+  bool hot = false;
+  if (my_valid) {
+    const float p = fexp2(s2 - st.M);
+    hot = !(k.gated && (s2 - (half ? mpreB : mpreA)) < k.log2tau);
     st.Lsum += p;
+    const float pw = p * kWScale;
 #pragma unroll
     for (int i = 0; i < NVG; ++i) {
       const uint32_t sz = cur.vsz[i];
-      const float wv = p * f16_lo(sz);
-      float cz = p * f16_hi(sz);
-      if (k.gated && !hot) cz = fmaf(1.5f, wv, cz);
-      st.Csum[i] += cz;
-      sm.wbuf[w][i][lane] = wv;
+      // Csum gathers p * z, plus p * 1.5 * s for a cold token (middle of its bucket)
+      const float zc = (k.gated && !hot) ? fmaf(1.5f, f16_lo(sz), f16_hi(sz)) : f16_hi(sz);
+      st.Csum[i] = fmaf(p, zc, st.Csum[i]);
+      sm.wbuf[w][i][lane] = fmaf(pw, f16_lo(sz), 0.f);   // kWScale * weight
     }
-    if (k.mask_row) k.mask_row[(size_t)grp * kGroup + lane] = hot ? 1 : 0;
+    if (k.mask_row) k.mask_row[(size_t)(gA + half) * kGroup + hl] = hot ? 1 : 0;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NVG; ++i) sm.wbuf[w][i][lane] = 0.f;
   }
-  const uint32_t hotmask = (uint32_t)__ballot(lane < kGroup && hot);
-  if (BITS == 4 && lane < kGroup && hot) sm.hot_list[w][__popc(hotmask & ((1u << lane) - 1u))] = lane;
+  const unsigned long long hotmask = __ballot(hot);
+  if (BITS == 4 && hot) {
+    const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(hotmask >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)hotmask, 0u));
+    sm.hot_list[w][pos] = lane;
+  }
   wave_lds_sync();
 
-  // ---- issue the low-plane loads of the hot tokens (accumulated next round)
+  // ---- low-plane loads of the hot tokens: the first 32 accumulate next round, any more now
   if (BITS == 4) {
-    const int nhot = __popc(hotmask);
+    const int nhot = __popcll(hotmask);
     st.hot += nhot;
-    const int lp0 = grp * (kGroup / P);
-    gbytes blk0 = page_block(r, lp0);
-    gbytes blk1 = P == kGroup ? blk0 : page_block(r, lp0 + 1);
+    const PairPages<P> pp = pair_pages<P>(r, gA, validB ? gA + 1 : gA);
+    const int slot = lane >> 3;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int idx = 8 * kk + tq8;
-      st.lo_wt[kk] = 0.f;
+    for (int kk = 0; kk < 8; ++kk) {
+      const int idx = 8 * kk + slot;
+      if (kk < 4) st.lo_wt[kk] = 0.f;
       if (8 * kk < nhot && idx < nhot) {
-        const int t = sm.hot_list[w][idx];
-        gbytes blk = t < P ? blk0 : blk1;
-        st.lo_word[kk] = gp<uint32_t>(blk + lay.vlo)[(t % P) * (kHeadDim / 16) + cbv];
-        st.lo_wt[kk] = 0.25f * sm.wbuf[w][vg_lane][t];
+        const int T = sm.hot_list[w][idx];
+        const int t = T & 31;
+        const uint32_t word = gp<uint32_t>(pp.lane_block(T >> 5, t) + lay.vlo)[(t % P) * (kHeadDim / 16) + cbv];
+        const float wo = sm.wbuf[w][vg_lane][T] * k.lo_scale;
+        if (kk < 4) {
+          st.lo_word[kk] = word;
+          st.lo_wt[kk] = wo;
+        } else {
+          add_lo(word, wo, st.acc);
+        }
       }
     }
   }
 
-  // ---- high plane (INT4) or codes (INT2) of all 32 tokens
+  // ---- high plane (INT4) or codes (INT2): 8 tokens of the lane's group, in 4 token pairs
   {
-    const float4 wt = *reinterpret_cast<const float4*>(&sm.wbuf[w][vg_lane][tq8 * 4]);
-    const uint32_t wd[4] = {cur.vc.x, cur.vc.y, cur.vc.z, cur.vc.w};
-    const float wf[4] = {wt.x, wt.y, wt.z, wt.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float x[16];
-      unpack16(wd[j], x);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.acc[i] = fmaf(wf[j], x[i], st.acc[i]);
-    }
+    const int tb = half * 32 + (hl >> 3) * 8;
+    const float4 wa = *reinterpret_cast<const float4*>(&sm.wbuf[w][vg_lane][tb]);
+    const float4 wb = *reinterpret_cast<const float4*>(&sm.wbuf[w][vg_lane][tb + 4]);
+    const half2v p0 = pack_h2(wa.x, wa.y);
+    const half2v p1 = pack_h2(wa.z, wa.w);
+    const half2v p2 = pack_h2(wb.x, wb.y);
+    const half2v p3 = pack_h2(wb.z, wb.w);
+    const uint32_t ones = k.mk.one;
+    st.W = dot2(p0, ones, st.W);
+    st.W = dot2(p1, ones, st.W);
+    st.W = dot2(p2, ones, st.W);
+    st.W = dot2(p3, ones, st.W);
+    dot2_pair(cur.vc[0].x, cur.vc[0].y, p0, k.mk, st.acc);
+    dot2_pair(cur.vc[0].z, cur.vc[0].w, p1, k.mk, st.acc);
+    dot2_pair(cur.vc[1].x, cur.vc[1].y, p2, k.mk, st.acc);
+    dot2_pair(cur.vc[1].z, cur.vc[1].w, p3, k.mk, st.acc);
   }
   wave_lds_sync();
 }
@@ -387,13 +504,22 @@ struct DecodeParams {
   DecodeCall c;
 };
 
+#ifndef LOOPKV_WAVES_PER_SIMD
+#define LOOPKV_WAVES_PER_SIMD 3
+#endif
+#if LOOPKV_WAVES_PER_SIMD > 0
+#define LKV_OCCUPANCY __attribute__((amdgpu_waves_per_eu(LOOPKV_WAVES_PER_SIMD, LOOPKV_WAVES_PER_SIMD)))
+#else
+#define LKV_OCCUPANCY
+#endif
+
 template <int BITS, int NVG, int P, int NW>
-__global__ __launch_bounds__(64 * NW) void decode_kernel(DecodeParams prm) {
+__global__ __launch_bounds__(64 * NW) LKV_OCCUPANCY void decode_kernel(DecodeParams prm) {
   const Geom& g = prm.g;
   const DecodeCall& c = prm.c;
   constexpr int KCH = 32 / BITS;
   constexpr int NCB = kHeadDim / KCH;
-  constexpr float VS = BITS == 4 ? 4.f : 1.f;   // true numerator = VS * acc + C
+  constexpr float VS = BITS == 4 ? 4.f : 1.f;   // value units of acc: true = VS * code
   static_assert(NW >= 2, "the final merge uses 128 threads");
   __shared__ Smem<NVG, NW> sm;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -447,15 +573,20 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(DecodeParams prm) {
   k.scale2 = c.sm_scale * kLog2e;
   k.log2tau = c.tau > 0.f ? log2f(c.tau) : -INFINITY;
   k.u = u;
+  k.lo_scale = inv_u * (1.f / kWScale);
   k.w = w;
   k.lane = lane;
   k.gs = gs;
   k.ge = ge;
   k.mask_row = c.mask ? c.mask + ((size_t)b * H + h) * c.mask_stride : nullptr;
+  k.mk.one = 0x3C003C00u;
+  k.mk.m89 = 0x03000300u;
+  k.mk.m67 = 0x00C000C0u;
 
   WaveState<NVG> st;
   st.M = -INFINITY;
   st.Lsum = 0.f;
+  st.W = 0.f;
   st.m_run = c.seed ? c.seed[(size_t)b * H + h] * kLog2e : -INFINITY;
   st.hot = 0;
 #pragma unroll
@@ -465,11 +596,14 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(DecodeParams prm) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { st.lo_word[i] = 0u; st.lo_wt[i] = 0.f; }
 
-  const int cb = lane % NCB;
+  const int cb = (lane & 31) % NCB;
   const int cbv = lane & 7, tq8 = lane >> 3;
-  const int rounds = (ge - gs + NW - 1) / NW;
-  GroupRegs<BITS, NVG> ra, rb;
-  if (gs + w < ge) load_group<BITS, NVG, P>(ra, r, lay, gs + w, lane);
+  const int rounds = (ge - gs + 2 * NW - 1) / (2 * NW);
+  PairRegs<BITS, NVG> ra, rb;
+  {
+    const int gA = gs + 2 * w;
+    if (gA < ge) load_pair<BITS, NVG, P>(ra, pair_pages<P>(r, gA, gA + 1 < ge ? gA + 1 : gA), lay, lane);
+  }
   __syncthreads();
 
   // The lane's query channels, scaled by 1/u (and by 1/4 for INT2 codes two bits up).
@@ -487,14 +621,8 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(DecodeParams prm) {
   // Low planes of the last round.
   if (BITS == 4) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (st.lo_wt[kk] != 0.f) {
-        float x[16];
-        unpack16(st.lo_word[kk], x);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st.acc[i] = fmaf(st.lo_wt[kk], x[i], st.acc[i]);
-      }
-    }
+    for (int kk = 0; kk < 4; ++kk)
+      if (st.lo_wt[kk] != 0.f) add_lo(st.lo_word[kk], st.lo_wt[kk], st.acc);
   }
 
   // Exact tail tokens (last split only), in chunks of 32, distributed over the waves.
@@ -518,29 +646,36 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(DecodeParams prm) {
             part = fmaf(sm.q[cbt * 8 + 2 * i + 1], bf16_hi(kk4[i]), part);
           }
         }
-        sm.red[w][cbt][t] = part;
+        sm.red[w][0][cbt][t] = part;
       }
       wave_lds_sync();
       float s2 = -INFINITY;
       if (lane < kGroup && ch * kGroup + lane < n_tail) {
         float raw = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < 16; ++cc) raw += sm.red[w][cc][lane];
+        for (int cc = 0; cc < 16; ++cc) raw += sm.red[w][0][cc][lane];
         s2 = raw * k.scale2;
       }
-      const float gm = wave_max(s2);
-      const float Mn = fmaxf(st.M, gm);
-      const float f = (st.M == -INFINITY) ? 0.f : exp2f(st.M - Mn);
-      st.M = Mn;
-      st.Lsum *= f;
+      const float gmx = wave_max(s2);
+      if (gmx > st.M) {
+        if (st.M != -INFINITY) {
+          const float f = fexp2(st.M - gmx);
+          st.Lsum *= f;
+          st.W *= f;
 #pragma unroll
-      for (int i = 0; i < NVG; ++i) st.Csum[i] *= f;
+          for (int i = 0; i < NVG; ++i) st.Csum[i] *= f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st.acc[i] *= f;
+          for (int i = 0; i < 16; ++i) st.acc[i] *= f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st.lo_wt[i] *= f;
+        }
+        st.M = gmx;
+      }
       if (lane < kGroup) {
-        const float p = (ch * kGroup + lane < n_tail) ? exp2f(s2 - st.M) : 0.f;
+        const float p = (ch * kGroup + lane < n_tail) ? fexp2(s2 - st.M) : 0.f;
         st.Lsum += p;
-        sm.wbuf[w][0][lane] = p * (u / VS);         // into scaled units (x u)
+        // odd-channel weight in offset units: (p / VS) * kWScale / 16; even channels 4x that
+        sm.wbuf[w][0][lane] = p * (kWScale / 16.f / VS);
       }
       wave_lds_sync();
       for (int j = 0; j < 4; ++j) {
@@ -554,9 +689,9 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(DecodeParams prm) {
         const float wt = sm.wbuf[w][0][t];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          // channel 2i is even (scale u), channel 2i+1 is odd (scale 4u)
-          st.acc[2 * i] = fmaf(wt, bf16_lo(vv[i]), st.acc[2 * i]);
-          st.acc[2 * i + 1] = fmaf(4.f * wt, bf16_hi(vv[i]), st.acc[2 * i + 1]);
+          // exact values, offset-free: even channels weigh 4x the odd ones (f = 1/4 vs 1/16)
+          st.acc[2 * i] = fmaf(4.f * wt, bf16_lo(vv[i]), st.acc[2 * i]);
+          st.acc[2 * i + 1] = fmaf(wt, bf16_hi(vv[i]), st.acc[2 * i + 1]);
         }
       }
       wave_lds_sync();
@@ -564,10 +699,14 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(DecodeParams prm) {
   }
 
   // Merge the waves: sum lanes, then combine the NW softmax states.
-  const float Lsum = wave_sum(lane < kGroup ? st.Lsum : 0.f);
+  const float Lsum = wave_sum(st.Lsum);
   float Csum[NVG];
 #pragma unroll
-  for (int i = 0; i < NVG; ++i) Csum[i] = wave_sum(lane < kGroup ? st.Csum[i] : 0.f);
+  for (int i = 0; i < NVG; ++i) Csum[i] = wave_sum(st.Csum[i]);
+  float W = st.W;
+  W += __shfl_xor(W, 8);
+  W += __shfl_xor(W, 16);
+  W += __shfl_xor(W, 32);
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -575,7 +714,8 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(DecodeParams prm) {
     v += __shfl_xor(v, 8);
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
-    acc[i] = v * ((i & 1) ? 0.25f * inv_u : inv_u);   // back from scaled units
+    // offset units: even channels carry code/4, odd code/16, weights x kWScale
+    acc[i] = (v - W) * ((i & 1) ? 16.f : 4.f) * (1.f / kWScale);
   }
   if (lane < 8) {
 #pragma unroll
@@ -642,10 +782,12 @@ __global__ __launch_bounds__(kHeadDim) void merge_kernel(Geom g, DecodeCall c) {
   c.out[row * kHeadDim + tid] = den > 0.f ? num / den : 0.f;
 }
 
-// Waves per workgroup: 3 lets four workgroups of the register budget these kernels use
-// (at most 168 VGPRs, three waves per SIMD) share a CU, so 4 (request, head) rows per CU run
-// in one generation.
-constexpr int kNW = 3;
+// Waves per workgroup, and the waves per SIMD the register allocation targets (0: compiler's
+// choice). Four (request, head) rows per CU keep a 1024-row launch in one generation.
+#ifndef LOOPKV_NW
+#define LOOPKV_NW 3
+#endif
+constexpr int kNW = LOOPKV_NW;
 
 template <int BITS, int P>
 hipError_t launch_bp(const Geom& g, const DecodeCall& c, hipStream_t stream) {
