@@ -83,13 +83,19 @@ def build_cache(name, seed, tau):
     return cache, plan, pt, pt_np, dict(layers=layers, loops=loops, B=B, N=N, split=split, heavy=heavy)
 
 
-def run_step(cache, plan, qs, outs, seq, pt, tau, split, stats=None):
+def run_step(cache, plan, qs, outs, seq, pt, tau, split, stats=None, events=None, stream=None):
+    """One decode step: every cell's decode launch in model order (loop-major). With `events`
+    (a list of len(cells) + 1), an event is recorded before the first launch and after each."""
     loops, layers = plan.shape
     i = 0
+    if events is not None:
+        events[0].record(stream)
     for t in range(loops):
         for l in range(layers):
             cache.decode(l, t, qs[i], seq, pt, tau=tau, split_tokens=split, out=outs[i],
                          stats=None if stats is None else stats[i])
+            if events is not None:
+                events[i + 1].record(stream)
             i += 1
 
 
@@ -114,12 +120,14 @@ def algorithmic_bytes(plan, hot_frac, B, N, H=16, n_split=1):
     return total, per_cell
 
 
-def cpu_baseline(cfg, plan, tau, seed, budget_s=15.0):
-    """The fp64 oracle on a bounded sample: for a few cells (INT4, INT2, reuse) and requests, the
-    oracle packs its own quantization of the same synthetic K/V into pages (untimed), then the
-    timed part reads the packed rows back, dequantizes, builds the fetch mask and runs fp64
-    attention. Extrapolated linearly in (token, head) rows to the whole step."""
-    import torch
+def cpu_baseline(cfg, plan, tau, seed, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the same workload, on one host core.
+
+    Untimed: for one request of one INT4, one INT2 and one reusing cell, the oracle quantizes the
+    same synthetic K/V the GPU was filled with and packs them into pages. Timed: decode of
+    (request, head) rows from those packed pages -- read the pages back, dequantize, build the
+    fetch mask, fp64 softmax attention -- cycling through the sampled rows with the step's
+    queries until `budget_s` is spent. Extrapolated linearly in rows to the whole step."""
     from threadpoolctl import threadpool_limits
 
     import oracle as O
@@ -132,40 +140,37 @@ def cpu_baseline(cfg, plan, tau, seed, budget_s=15.0):
         idx = np.argwhere(plan == code)
         if len(idx):
             cells.append(tuple(int(x) for x in idx[0]))
-    rows_done = 0
-    timed = 0.0
-    reqs = [0]
+    rows = []
     with threadpool_limits(limits=1):
         for (t, l) in cells:
             st, sl = (loops - 1, l) if plan[t, l] == 0 else (t, l)
             bits = int(plan[st, sl])
             cs = seed * 100003 + st * 1000 + sl
-            # the same generator as the GPU fill, then the sampled request copied to the host
-            k = synth.keys(B, N, H, 128, cs, device="cuda", heavy_tail=cfg["heavy"])[reqs].double().cpu().numpy()
-            v = synth.values(B, N, H, 128, cs, device="cuda")[reqs].double().cpu().numpy()
-            q = synth.queries(B, H, 128, 777 + t * 100 + l, device="cuda")[reqs].double().cpu().numpy()
-            for bi in range(len(reqs)):
-                heads = [O.quantize_head(k[bi, :, h], v[bi, :, h], bits, 128) for h in range(H)]
-                pt = np.arange(N // 32)[None, :]
-                pool = O.pack_pool(bits, 32, [heads], pt, N // 32)
-                for h in range(H):
-                    t0 = time.perf_counter()
-                    qh = O.unpack_pool_head(bits, 32, pool, pt[0], N, h, H)
-                    O.decode_head(q[bi, h], qh, np.zeros((0, 128)), np.zeros((0, 128)),
-                                  sm_scale=1 / math.sqrt(128), tau=tau, split_tokens=cfg["split"])
-                    timed += time.perf_counter() - t0
-                    rows_done += 1
-                    if timed > budget_s:
-                        break
-                if timed > budget_s:
-                    break
+            # the generator of the GPU fill; request 0 copied to the host
+            k = synth.keys(B, N, H, 128, cs, device="cuda", heavy_tail=cfg["heavy"])[0].double().cpu().numpy()
+            v = synth.values(B, N, H, 128, cs, device="cuda")[0].double().cpu().numpy()
+            q = synth.queries(B, H, 128, 777 + t * 100 + l, device="cuda").double().cpu().numpy()
+            heads = [O.quantize_head(k[:, h], v[:, h], bits, 128) for h in range(H)]
+            pt = np.arange(N // 32)[None, :]
+            pool = O.pack_pool(bits, 32, [heads], pt, N // 32)
+            for h in range(H):
+                rows.append((bits, pool, pt[0], h, q[:, h]))
+        timed, done = 0.0, 0
+        e = np.zeros((0, 128))
+        while timed < budget_s:
+            bits, pool, ptr, h, qs = rows[done % len(rows)]
+            t0 = time.perf_counter()
+            qh = O.unpack_pool_head(bits, 32, pool, ptr, N, h, H)
+            O.decode_head(qs[done % B], qh, e, e, sm_scale=1 / math.sqrt(128), tau=tau,
+                          split_tokens=cfg["split"])
+            timed += time.perf_counter() - t0
+            done += 1
     rows_step = loops * layers * B * H
-    per_row = timed / rows_done
-    us_step = per_row * rows_step * 1e6
-    return {"value": us_step, "unit": "us/step", "cores": 1, "kind": "oracle",
-            "sample": f"{rows_done} (request, head) rows of {len(cells)} cells (INT4 / INT2 / reuse), "
-                      f"{N} tokens each, {timed:.1f} s timed; extrapolated x{rows_step / rows_done:.0f} "
-                      f"to {rows_step} rows per step"}
+    us_step = timed / done * rows_step * 1e6
+    return {"value": round(us_step, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
+            "sample": f"{done} (request, head) decodes of {N} tokens from {len(rows)} packed rows of "
+                      f"{len(cells)} cells (INT4 / INT2 / reuse), {timed:.1f} s on one core; "
+                      f"extrapolated x{rows_step / done:.0f} to the {rows_step} rows of one step"}
 
 
 def main():
@@ -216,27 +221,40 @@ def main():
         torch.cuda.synchronize()
         del x, y
 
+    # The library launches on torch's current stream, so its events bracket the kernels.
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         run_step(cache, plan, qs, outs, seq, pt, args.tau, split)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    ev[0].record(stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ncell + 1)] for _ in range(args.steps)]
+    t_wall = time.perf_counter()
     for i in range(args.steps):
-        run_step(cache, plan, qs, outs, seq, pt, args.tau, split)
-        ev[i + 1].record(stream)
+        run_step(cache, plan, qs, outs, seq, pt, args.tau, split, events=ev[i], stream=stream)
     torch.cuda.synchronize()
-    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
-    total_ms = ev[0].elapsed_time(ev[-1])
+    t_wall = time.perf_counter() - t_wall
+    step_ms = np.array([ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)])
+    launch_ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(ncell)]
+                          for i in range(args.steps)])              # [step, cell]
+    total_ms = ev[0][0].elapsed_time(ev[-1][-1])
     med_ms = float(np.median(step_ms))
     for o in outs:
         assert torch.isfinite(o).all()
 
     n_split = (N + split - 1) // split if split else 1
-    alg_bytes, _ = algorithmic_bytes(plan, hot_frac, B, N, n_split=n_split)
-    per_launch_bytes = alg_bytes / ncell
-    per_launch_s = med_ms / 1e3 / ncell
-    achieved = per_launch_bytes / per_launch_s / 1e9
+    alg_bytes, per_cell_bytes = algorithmic_bytes(plan, hot_frac, B, N, n_split=n_split)
+    # Dominant kernel: the INT4-read decode (own INT4 cells and cells reusing an INT4 source).
+    src_bits = np.array([plan[loops - 1, l] if plan[t, l] == 0 else plan[t, l]
+                         for t in range(loops) for l in range(layers)])
+    kinds = {}
+    for bits in (4, 2):
+        sel = src_bits == bits
+        if sel.any():
+            dur = float(launch_ms[:, sel].mean())                    # ms per launch
+            byt = float(np.asarray(per_cell_bytes)[sel].mean())      # bytes per launch
+            kinds[bits] = dict(launches_per_step=int(sel.sum()), avg_us=round(dur * 1e3, 1),
+                               bytes_per_launch=int(byt), GBps=round(byt / (dur / 1e3) / 1e9, 1))
+    dom = max(kinds, key=lambda b: kinds[b]["avg_us"] * kinds[b]["launches_per_step"])
+    achieved = kinds[dom]["GBps"]
 
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "decode_traffic.json")
@@ -272,7 +290,10 @@ def main():
         "hot_fraction": round(overall_hot, 4),
         "alg_bytes_per_step": int(alg_bytes),
         "mean_ms_per_step": round(total_ms / args.steps, 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+        "wall_s_timed": round(t_wall, 3),
+        "kernels": {f"decode_int{b}_read": v for b, v in kinds.items()},
+        "roofline": {"bound": "hbm", "kernel": f"decode_kernel<{dom},...> (INT{dom}-read cells)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         "kernel_hash": kernel_hash(),
