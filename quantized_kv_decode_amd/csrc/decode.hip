@@ -90,17 +90,28 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ float dpp_max(float v, int ctrl_dummy);
+// max(a, b) as one v_max_f32. The values here are scores or -inf, never NaN, so the NaN
+// quieting that fmaxf adds to every operand is not needed.
+__device__ __forceinline__ float dmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float dmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
 // Maximum within each 16-lane row, broadcast to the row.
 __device__ __forceinline__ float row_max16(float v) {
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                   0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));   // quad xor 1
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                   0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));   // quad xor 2
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                   0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));  // half-row mirror
-  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                   0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));  // row mirror
+  v = dmax(v, dpp_mov<0xB1>(v));    // quad xor 1
+  v = dmax(v, dpp_mov<0x4E>(v));    // quad xor 2
+  v = dmax(v, dpp_mov<0x141>(v));   // half-row mirror
+  v = dmax(v, dpp_mov<0x140>(v));   // row mirror
   return v;
 }
 __device__ __forceinline__ float lane_f(float v, int l) {
@@ -381,28 +392,29 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   float gmA = -INFINITY, gmB = -INFINITY;
   if (active) {
     const float rm = row_max16(s2);
-    gmA = fmaxf(lane_f(rm, 0), lane_f(rm, 16));
-    gmB = fmaxf(lane_f(rm, 32), lane_f(rm, 48));
+    gmA = dmax(lane_f(rm, 0), lane_f(rm, 16));
+    gmB = dmax(lane_f(rm, 32), lane_f(rm, 48));
   }
   if (lane == 0) {
     sm.gmax[rd & 1][w][0] = gmA;
     sm.gmax[rd & 1][w][1] = gmB;
   }
   __syncthreads();
-  float mpreA = st.m_run, mall = st.m_run;
+  // Group maxima of this round in stream order: wave i's groups are 2i and 2i+1.
+  const float* gx = &sm.gmax[rd & 1][0][0];
+  float mall = st.m_run;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const float x0 = sm.gmax[rd & 1][i][0], x1 = sm.gmax[rd & 1][i][1];
-    if (i <= w) mpreA = fmaxf(mpreA, x0);
-    if (i < w) mpreA = fmaxf(mpreA, x1);
-    mall = fmaxf(mall, fmaxf(x0, x1));
-  }
-  const float mpreB = fmaxf(mpreA, gmB);
+  for (int j = 0; j < 2 * NW; j += 2) mall = dmax3(mall, gx[j], gx[j + 1]);
+  float mpreA = dmax(st.m_run, gx[0]);      // everything up to this wave's first group
+#pragma unroll
+  for (int i = 1; i < NW; ++i)
+    if (i <= w) mpreA = dmax3(mpreA, gx[2 * i - 1], gx[2 * i]);
+  const float mpreB = dmax(mpreA, gmB);
   st.m_run = mall;
   if (!active) return;
 
   // ---- online softmax: rescale only when the wave's maximum grows
-  const float gm = fmaxf(gmA, gmB);
+  const float gm = dmax(gmA, gmB);
   if (gm > st.M) {
     if (st.M != -INFINITY) {
       const float f = fexp2(st.M - gm);
