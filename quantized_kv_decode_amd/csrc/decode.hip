@@ -340,16 +340,19 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   const bool validB = gA + 1 < k.ge;
   const bool my_valid = half ? validB : active;
   {
-    const int nA = gA + 2 * NW;
-    if (nA < k.ge) {
-      const int nB = nA + 1 < k.ge ? nA + 1 : nA;   // never index past the history
-      load_pair<BITS, NVG, P>(nxt, pair_pages<P>(r, nA, nB), lay, lane);
-    }
+    // Issued on every round, also when the wave has no next pair (then it re-reads the split's
+    // last group, which is cached): with a fixed number of loads per round the wait before
+    // this round's data can leave the next round's loads in flight.
+    const int nA = min(gA + 2 * NW, k.ge - 1);
+    const int nB = min(nA + 1, k.ge - 1);
+    load_pair<BITS, NVG, P>(nxt, pair_pages<P>(r, nA, nB), lay, lane);
   }
 
   // ---- scores of both groups (key codes read first, section 3.3)
-  float s2 = -INFINITY;
-  if (active) {
+  // Every step below runs also on a wave without groups this round (its scores are -inf and
+  // its weights 0): then every path through the round consumes the same loads.
+  float s2;
+  {
     float qs[KCH], ke = 0.f, ko = 0.f;
     const uint32_t* kszw = reinterpret_cast<const uint32_t*>(cur.ksz);
 #pragma unroll
@@ -389,12 +392,9 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
     for (int kk = 0; kk < NCB; ++kk) raw += sm.red[w][half][kk][hl];
     s2 = my_valid ? raw * k.scale2 : -INFINITY;
   }
-  float gmA = -INFINITY, gmB = -INFINITY;
-  if (active) {
-    const float rm = row_max16(s2);
-    gmA = dmax(lane_f(rm, 0), lane_f(rm, 16));
-    gmB = dmax(lane_f(rm, 32), lane_f(rm, 48));
-  }
+  const float rm = row_max16(s2);
+  const float gmA = dmax(lane_f(rm, 0), lane_f(rm, 16));
+  const float gmB = dmax(lane_f(rm, 32), lane_f(rm, 48));
   if (lane == 0) {
     sm.gmax[rd & 1][w][0] = gmA;
     sm.gmax[rd & 1][w][1] = gmB;
@@ -411,7 +411,6 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
     if (i <= w) mpreA = dmax3(mpreA, gx[2 * i - 1], gx[2 * i]);
   const float mpreB = dmax(mpreA, gmB);
   st.m_run = mall;
-  if (!active) return;
 
   // ---- online softmax: rescale only when the wave's maximum grows
   const float gm = dmax(gmA, gmB);
@@ -468,7 +467,9 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   if (BITS == 4) {
     const int nhot = __popcll(hotmask);
     st.hot += nhot;
-    const PairPages<P> pp = pair_pages<P>(r, gA, validB ? gA + 1 : gA);
+    // (a wave without groups this round has no hot tokens; its lookup stays inside the history)
+    const int cA = min(gA, k.ge - 1);
+    const PairPages<P> pp = pair_pages<P>(r, cA, validB ? cA + 1 : cA);
     const int slot = lane >> 3;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
