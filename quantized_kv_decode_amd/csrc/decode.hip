@@ -188,9 +188,10 @@ __device__ __forceinline__ void dot2_pair(uint32_t w0, uint32_t w1, half2v wp, c
 template <int NVG, int NW>
 struct Smem {
   alignas(16) float q[kHeadDim];
+  alignas(16) float qv[kHeadDim];         // q / u, odd INT2 channels / (4u): the key operand
   alignas(16) float red[NW][2][16][36];   // per-wave key partials [half][channel block][token]
   alignas(16) float wbuf[NW][NVG][64];    // per-wave value weights [value group][token of pair]
-  int hot_list[NW][64];
+  int2 hot_list[NW][64];                  // hot tokens of the round: (token of pair, page id)
   float gmax[2][NW][2];
   float fin_acc[NW][kHeadDim];
   float fin_M[NW], fin_L[NW], fin_C[NW][NVG];
@@ -206,83 +207,100 @@ struct PairRegs {
   u32x4 ksz[KSW];
   u32x4 vc[2];
   uint32_t vsz[NVG];
+  int pid;          // page holding the lane's token (its low plane is read from there)
 };
 
 struct RowCtx {
-  gbytes pool;
-  int64_t page_bytes;
-  const LKV_CONST int32_t* pt_row;
-  int64_t head_off;
-  int64_t num_pages;
+  gbytes pool;                      // read pool, advanced to this head's block in page 0
+  uint32_t page_bytes;
+  uint32_t num_pages;
+  const LKV_GLOBAL int32_t* pt_row;
   uint32_t* err;
 };
 
-__device__ __forceinline__ gbytes page_block(const RowCtx& r, int logical_page) {
-  int pid = r.pt_row[logical_page];
-  if (pid < 0 || pid >= r.num_pages) {
-    atomicOr(r.err, (uint32_t)kErrPage);
-    pid = 0;
-  }
-  return r.pool + (int64_t)pid * r.page_bytes + r.head_off;
-}
-
-// Page blocks of a pair of groups: [group of the pair][page within the group].
-template <int P>
-struct PairPages {
-  gbytes b[2][2];
-  __device__ __forceinline__ gbytes lane_block(int half, int t) const {
-    gbytes g0 = half ? b[1][0] : b[0][0];
-    if (P == kGroup) return g0;
-    gbytes g1 = half ? b[1][1] : b[0][1];
-    return t < P ? g0 : g1;
-  }
+// Page ids a lane needs for one pair of groups: the page holding its token (lanes 0..31 take
+// the pair's first group, lanes 32..63 the second) and, with 16-token pages, the group's first
+// page, which holds the key scales. They are loaded a round before the pair's data.
+struct LaneIds {
+  int tok, first;
 };
 
 template <int P>
-__device__ __forceinline__ PairPages<P> pair_pages(const RowCtx& r, int gA, int gB) {
-  PairPages<P> pp;
+__device__ __forceinline__ LaneIds load_ids(const RowCtx& r, int g, int ge, int lane) {
   constexpr int PPG = kGroup / P;   // pages per group
-  pp.b[0][0] = page_block(r, gA * PPG);
-  pp.b[1][0] = page_block(r, gB * PPG);
-  if (PPG == 2) {
-    pp.b[0][1] = page_block(r, gA * PPG + 1);
-    pp.b[1][1] = page_block(r, gB * PPG + 1);
-  } else {
-    pp.b[0][1] = pp.b[0][0];
-    pp.b[1][1] = pp.b[1][0];
-  }
-  return pp;
+  const int gg = min(g + (lane >> 5), ge - 1);   // never past the history
+  LaneIds id;
+  id.tok = r.pt_row[gg * PPG + (PPG == 2 ? ((lane >> 4) & 1) : 0)];
+  id.first = PPG == 2 ? r.pt_row[gg * PPG] : id.tok;
+  return id;
 }
 
+// A page id outside the pool is reported and replaced by page 0.
+__device__ __forceinline__ int checked_page(const RowCtx& r, int pid) {
+  if ((uint32_t)pid >= r.num_pages) {
+    atomicOr(r.err, (uint32_t)kErrPage);
+    pid = 0;
+  }
+  return pid;
+}
+__device__ __forceinline__ gbytes page_at(const RowCtx& r, int pid) {
+  return r.pool + (uint64_t)(uint32_t)pid * r.page_bytes;
+}
+
+// Byte offsets of a lane's loads inside its head block (fixed for the kernel).
+struct LaneOffs {
+  uint32_t kc, ksz, vc, vsz;
+};
+
 template <int BITS, int NVG, int P>
-__device__ __forceinline__ void load_pair(PairRegs<BITS, NVG>& g, const PairPages<P>& pp,
-                                          const Layout& lay, int lane) {
+__device__ __forceinline__ LaneOffs lane_offsets(const Layout& lay, int lane) {
   constexpr int KCH = 32 / BITS;
   constexpr int NCB = kHeadDim / KCH;
   constexpr int KTOK = NCB;                 // tokens per lane in a 32-lane half
-  const int half = lane >> 5, hl = lane & 31;
+  const int hl = lane & 31;
   const int cb = hl % NCB, t0 = (hl / NCB) * KTOK;
-  {  // key codes of KTOK tokens of channel block cb
-    const LKV_GLOBAL u32x4* p = gp<u32x4>(pp.lane_block(half, t0) + lay.kc + 4 * (cb * P + t0 % P));
+  const int cbv = hl & 7, tv = (hl >> 3) * 8;
+  LaneOffs o;
+  o.kc = lay.kc + 4 * (cb * P + t0 % P);         // key codes of KTOK tokens of block cb
+  o.ksz = lay.ksz + 4 * cb * KCH;                // key (s, z) of the lane's channels
+  o.vc = lay.vc + 4 * (cbv * P + tv % P);        // value codes / high plane: 16 ch x 8 tokens
+  o.vsz = lay.vsz + 4 * (hl % P) * NVG;          // value (s, z) of token hl
+  return o;
+}
+
+template <int BITS, int NVG>
+__device__ __forceinline__ void load_pair(PairRegs<BITS, NVG>& g, gbytes tok_page, gbytes first_page,
+                                          const LaneOffs& o) {
+  {
+    const LKV_GLOBAL u32x4* p = gp<u32x4>(tok_page + o.kc);
 #pragma unroll
     for (int i = 0; i < PairRegs<BITS, NVG>::KCW; ++i) g.kc[i] = p[i];
   }
-  {  // key (s, z) of the lane's channels, stored with the group's first page
-    const LKV_GLOBAL u32x4* p = gp<u32x4>(pp.lane_block(half, 0) + lay.ksz + 4 * cb * KCH);
+  {
+    const LKV_GLOBAL u32x4* p = gp<u32x4>(first_page + o.ksz);
 #pragma unroll
     for (int i = 0; i < PairRegs<BITS, NVG>::KSW; ++i) g.ksz[i] = p[i];
   }
-  {  // value codes / high plane: 16 channels x 8 tokens
-    const int cbv = hl & 7, tv = (hl >> 3) * 8;
-    const LKV_GLOBAL u32x4* p = gp<u32x4>(pp.lane_block(half, tv) + lay.vc + 4 * (cbv * P + tv % P));
+  {
+    const LKV_GLOBAL u32x4* p = gp<u32x4>(tok_page + o.vc);
     g.vc[0] = p[0];
     g.vc[1] = p[1];
   }
-  {  // value (s, z) of token hl
-    const LKV_GLOBAL uint32_t* p = gp<uint32_t>(pp.lane_block(half, hl) + lay.vsz) + (hl % P) * NVG;
+  {
+    const LKV_GLOBAL uint32_t* p = gp<uint32_t>(tok_page + o.vsz);
 #pragma unroll
     for (int i = 0; i < NVG; ++i) g.vsz[i] = p[i];
   }
+}
+
+// Issues the loads of the pair whose lane page ids are `id`.
+template <int BITS, int NVG, int P>
+__device__ __forceinline__ void fetch_pair(PairRegs<BITS, NVG>& g, const RowCtx& r, const LaneIds& id,
+                                           const LaneOffs& o) {
+  const int tp = checked_page(r, id.tok);
+  const int fp = P == kGroup ? tp : checked_page(r, id.first);
+  g.pid = tp;
+  load_pair<BITS, NVG>(g, page_at(r, tp), page_at(r, fp), o);
 }
 
 // Softmax and value accumulation state of one wave.
@@ -325,8 +343,8 @@ __device__ __forceinline__ void add_lo(uint32_t word, float wo, float (&acc)[16]
 template <int BITS, int NVG, int P, int NW>
 __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st,
                                            const PairRegs<BITS, NVG>& cur, PairRegs<BITS, NVG>& nxt,
-                                           const RowCtx& r, const Layout& lay, const RoundConst& k,
-                                           const float (&qv)[32 / BITS], int rd) {
+                                           LaneIds& nid, const RowCtx& r, const LaneOffs& lo,
+                                           const RoundConst& k, int rd) {
   constexpr int KCH = 32 / BITS;
   constexpr int NCB = kHeadDim / KCH;
   constexpr int KTOK = NCB;
@@ -340,12 +358,22 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   const bool validB = gA + 1 < k.ge;
   const bool my_valid = half ? validB : active;
   {
-    // Issued on every round, also when the wave has no next pair (then it re-reads the split's
-    // last group, which is cached): with a fixed number of loads per round the wait before
-    // this round's data can leave the next round's loads in flight.
-    const int nA = min(gA + 2 * NW, k.ge - 1);
-    const int nB = min(nA + 1, k.ge - 1);
-    load_pair<BITS, NVG, P>(nxt, pair_pages<P>(r, nA, nB), lay, lane);
+    // The next pair's loads (page ids read last round) and the page ids of the pair after it.
+    // Both are issued on every round, also when the wave has no next pair (then it re-reads
+    // the split's last group, which is cached): with a fixed number of loads per round the
+    // wait before this round's data leaves the next round's loads in flight.
+    const LaneIds id = nid;
+    nid = load_ids<P>(r, gA + 4 * NW, k.ge, lane);
+    fetch_pair<BITS, NVG, P>(nxt, r, id, lo);
+  }
+  float qv[KCH];   // the lane's key operand (q / u), re-read from LDS to spare registers
+  {
+    const float4* qp = reinterpret_cast<const float4*>(&sm.qv[cb * KCH]);
+#pragma unroll
+    for (int i = 0; i < KCH / 4; ++i) {
+      const float4 v = qp[i];
+      qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
+    }
   }
 
   // ---- scores of both groups (key codes read first, section 3.3)
@@ -459,7 +487,7 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   if (BITS == 4 && hot) {
     const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(hotmask >> 32),
                                               __builtin_amdgcn_mbcnt_lo((uint32_t)hotmask, 0u));
-    sm.hot_list[w][pos] = lane;
+    sm.hot_list[w][pos] = make_int2(lane, cur.pid);
   }
   wave_lds_sync();
 
@@ -467,18 +495,16 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   if (BITS == 4) {
     const int nhot = __popcll(hotmask);
     st.hot += nhot;
-    // (a wave without groups this round has no hot tokens; its lookup stays inside the history)
-    const int cA = min(gA, k.ge - 1);
-    const PairPages<P> pp = pair_pages<P>(r, cA, validB ? cA + 1 : cA);
     const int slot = lane >> 3;
+    constexpr Layout lay = head_layout(BITS, P, kHeadDim, NVG);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int idx = 8 * kk + slot;
       if (kk < 4) st.lo_wt[kk] = 0.f;
       if (8 * kk < nhot && idx < nhot) {
-        const int T = sm.hot_list[w][idx];
-        const int t = T & 31;
-        const uint32_t word = gp<uint32_t>(pp.lane_block(T >> 5, t) + lay.vlo)[(t % P) * (kHeadDim / 16) + cbv];
+        const int2 e = sm.hot_list[w][idx];
+        const int T = e.x, t = T & 31;
+        const uint32_t word = gp<uint32_t>(page_at(r, e.y) + lay.vlo)[(t % P) * (kHeadDim / 16) + cbv];
         const float wo = sm.wbuf[w][vg_lane][T] * k.lo_scale;
         if (kk < 4) {
           st.lo_word[kk] = word;
@@ -545,7 +571,10 @@ __global__ __launch_bounds__(64 * NW) LKV_OCCUPANCY void decode_kernel(DecodePar
 
   if (tid < kHeadDim) {
     const uint16_t qb = c.q[((size_t)b * H + h) * kHeadDim + tid];
-    sm.q[tid] = __uint_as_float((uint32_t)qb << 16);
+    const float q = __uint_as_float((uint32_t)qb << 16);
+    sm.q[tid] = q;
+    // key operand: q / u, and q / (4u) on odd INT2 channels (their codes sit two bits up)
+    sm.qv[tid] = (BITS == 2 && (tid & 1)) ? q * 0.25f * inv_u : q * inv_u;
   }
   if (tid == 0) sm.cnt_hot = 0;
 
@@ -572,14 +601,13 @@ __global__ __launch_bounds__(64 * NW) LKV_OCCUPANCY void decode_kernel(DecodePar
   }
   const bool do_tail = split == c.n_split - 1 && n_tail > 0;
 
+  constexpr Layout lay = head_layout(BITS, P, kHeadDim, NVG);
   RowCtx r;
-  r.pool = as_global((const uint8_t*)d->read_pool);
-  r.page_bytes = d->read_page_bytes;
-  r.pt_row = as_const(c.page_table) + (size_t)b * c.pt_stride;
-  r.num_pages = g.num_pages;
+  r.pool = as_global((const uint8_t*)d->read_pool) + (size_t)h * lay.total;
+  r.page_bytes = (uint32_t)d->read_page_bytes;
+  r.num_pages = (uint32_t)min(g.num_pages, (int64_t)INT32_MAX);
+  r.pt_row = as_global(c.page_table) + (size_t)b * c.pt_stride;
   r.err = g.err;
-  const Layout lay = head_layout(BITS, P, kHeadDim, NVG);
-  r.head_off = (int64_t)h * lay.total;
 
   RoundConst k;
   k.gated = d->gated != 0;
@@ -609,27 +637,21 @@ __global__ __launch_bounds__(64 * NW) LKV_OCCUPANCY void decode_kernel(DecodePar
 #pragma unroll
   for (int i = 0; i < 4; ++i) { st.lo_word[i] = 0u; st.lo_wt[i] = 0.f; }
 
-  const int cb = (lane & 31) % NCB;
   const int cbv = lane & 7, tq8 = lane >> 3;
   const int rounds = (ge - gs + 2 * NW - 1) / (2 * NW);
+  const LaneOffs offs = lane_offsets<BITS, NVG, P>(lay, lane);
   PairRegs<BITS, NVG> ra, rb;
-  {
+  LaneIds nid{0, 0};   // page ids of the pair after the one in flight
+  if (rounds > 0) {
     const int gA = gs + 2 * w;
-    if (gA < ge) load_pair<BITS, NVG, P>(ra, pair_pages<P>(r, gA, gA + 1 < ge ? gA + 1 : gA), lay, lane);
+    fetch_pair<BITS, NVG, P>(ra, r, load_ids<P>(r, gA, ge, lane), offs);
+    nid = load_ids<P>(r, gA + 2 * NW, ge, lane);
   }
   __syncthreads();
 
-  // The lane's query channels, scaled by 1/u (and by 1/4 for INT2 codes two bits up).
-  float qv[KCH];
-#pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const float q = sm.q[cb * KCH + i];
-    qv[i] = (BITS == 2 && (i & 1)) ? q * 0.25f * inv_u : q * inv_u;
-  }
-
   for (int rd = 0; rd < rounds; rd += 2) {
-    round_body<BITS, NVG, P, NW>(sm, st, ra, rb, r, lay, k, qv, rd);
-    if (rd + 1 < rounds) round_body<BITS, NVG, P, NW>(sm, st, rb, ra, r, lay, k, qv, rd + 1);
+    round_body<BITS, NVG, P, NW>(sm, st, ra, rb, nid, r, offs, k, rd);
+    if (rd + 1 < rounds) round_body<BITS, NVG, P, NW>(sm, st, rb, ra, nid, r, offs, k, rd + 1);
   }
   // Low planes of the last round.
   if (BITS == 4) {

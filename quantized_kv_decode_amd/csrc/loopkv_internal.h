@@ -40,8 +40,8 @@ struct Layout {
   int32_t ksz, kc, vc, vsz, vlo, total;
 };
 
-__host__ __device__ inline Layout head_layout(int bits, int page_tokens, int head_dim, int nvg) {
-  Layout l;
+__host__ __device__ constexpr Layout head_layout(int bits, int page_tokens, int head_dim, int nvg) {
+  Layout l{};
   l.ksz = 0;
   l.kc = 4 * head_dim;
   l.vc = l.kc + page_tokens * head_dim * bits / 8;
