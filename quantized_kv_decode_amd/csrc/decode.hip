@@ -552,18 +552,25 @@ struct DecodeParams {
 #define LKV_OCCUPANCY
 #endif
 
-template <int BITS, int NVG, int P, int NW>
-__global__ __launch_bounds__(64 * NW) LKV_OCCUPANCY void decode_kernel(DecodeParams prm) {
+template <int BITS, int NVG, int P, int NW, int RB>
+__global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(DecodeParams prm) {
   const Geom& g = prm.g;
   const DecodeCall& c = prm.c;
   constexpr int KCH = 32 / BITS;
   constexpr int NCB = kHeadDim / KCH;
   constexpr float VS = BITS == 4 ? 4.f : 1.f;   // value units of acc: true = VS * code
   static_assert(NW >= 2, "the final merge uses 128 threads");
-  __shared__ Smem<NVG, NW> sm;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // RB rows (heads of one request) per workgroup, NW waves each. The rows share the round
+  // barrier, which keeps every wave of the CU at the same round: the SIMDs' oldest-first issue
+  // would otherwise run the workgroups one after another and leave the last alone on the CU.
+  __shared__ Smem<NVG, NW> sm_rows[RB];
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int rsub = wave / NW;
+  Smem<NVG, NW>& sm = sm_rows[rsub];
+  const int w = wave - rsub * NW;
+  const int split = blockIdx.x, h = blockIdx.y * RB + rsub, b = blockIdx.z;
+  const int tid = (int)threadIdx.x - rsub * 64 * NW;   // thread index among the row's waves
+  const int lane = tid & 63;
   const LKV_CONST CellDesc* d = as_const(c.desc_dev);
   const int H = g.H;
   const float u = cvt2<false>(1u).x;            // value of fp8 byte 0x01
@@ -824,17 +831,25 @@ __global__ __launch_bounds__(kHeadDim) void merge_kernel(Geom g, DecodeCall c) {
 #endif
 constexpr int kNW = LOOPKV_NW;
 
-template <int BITS, int P>
-hipError_t launch_bp(const Geom& g, const DecodeCall& c, hipStream_t stream) {
+template <int BITS, int P, int RB>
+hipError_t launch_bpr(const Geom& g, const DecodeCall& c, hipStream_t stream) {
   DecodeParams prm{g, c};
-  const dim3 grid((unsigned)c.n_split, (unsigned)g.H, (unsigned)c.batch);
+  const dim3 grid((unsigned)c.n_split, (unsigned)(g.H / RB), (unsigned)c.batch);
+  const unsigned threads = 64 * kNW * RB;
   switch (g.nvg) {
-    case 1: decode_kernel<BITS, 1, P, kNW><<<grid, 64 * kNW, 0, stream>>>(prm); break;
-    case 2: decode_kernel<BITS, 2, P, kNW><<<grid, 64 * kNW, 0, stream>>>(prm); break;
-    case 4: decode_kernel<BITS, 4, P, kNW><<<grid, 64 * kNW, 0, stream>>>(prm); break;
+    case 1: decode_kernel<BITS, 1, P, kNW, RB><<<grid, threads, 0, stream>>>(prm); break;
+    case 2: decode_kernel<BITS, 2, P, kNW, RB><<<grid, threads, 0, stream>>>(prm); break;
+    case 4: decode_kernel<BITS, 4, P, kNW, RB><<<grid, threads, 0, stream>>>(prm); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Four heads per workgroup when the head count allows (one workgroup per CU at 3 waves per
+// SIMD), else one.
+template <int BITS, int P>
+hipError_t launch_bp(const Geom& g, const DecodeCall& c, hipStream_t stream) {
+  return g.H % 4 == 0 ? launch_bpr<BITS, P, 4>(g, c, stream) : launch_bpr<BITS, P, 1>(g, c, stream);
 }
 
 }  // namespace
