@@ -190,8 +190,11 @@ struct Smem {
   alignas(16) float q[kHeadDim];
   alignas(16) float qv[kHeadDim];         // q / u, odd INT2 channels / (4u): the key operand
   alignas(16) float red[NW][2][16][36];   // per-wave key partials [half][channel block][token]
-  alignas(16) float wbuf[NW][NVG][64];    // per-wave value weights [value group][token of pair]
-  int2 hot_list[NW][64];                  // hot tokens of the round: (token of pair, page id)
+  // Per-wave value weights [round parity][wave][value group][token of pair] and hot tokens
+  // (token of pair, page id); the low planes of a round are added in the next one, which reads
+  // that round's copies.
+  alignas(16) float wbuf[2][NW][NVG][64];
+  int2 hot_list[2][NW][64];
   float gmax[2][NW][2];
   float fin_acc[NW][kHeadDim];
   float fin_M[NW], fin_L[NW], fin_C[NW][NVG];
@@ -244,7 +247,12 @@ __device__ __forceinline__ int checked_page(const RowCtx& r, int pid) {
   return pid;
 }
 __device__ __forceinline__ gbytes page_at(const RowCtx& r, int pid) {
-  return r.pool + (uint64_t)(uint32_t)pid * r.page_bytes;
+  // pid * page_bytes as one 32x32->64 multiply whose scalar operand is the page size; the
+  // pool base (also scalar) is added separately, so it never has to live in vector registers.
+  uint64_t off, carry;
+  asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(off), "=s"(carry) : "v"(pid), "s"(r.page_bytes));
+  (void)carry;
+  return r.pool + off;
 }
 
 // Byte offsets of a lane's loads inside its head block (fixed for the kernel).
@@ -313,8 +321,9 @@ struct WaveState {
   // (odd i), and W collects the w'; low planes and exact tail values are added without the
   // offset. True weighted sum of channel i = (acc[i] - W) / (f_i * kWScale).
   float acc[16];
-  uint32_t lo_word[4];           // low planes loaded last round
-  float lo_wt[4];                // their odd-channel weights (0: nothing loaded)
+  uint32_t lo_word[8];           // low planes of last round's hot tokens
+  int nlo;                       // last round's hot count
+  float lo_f;                    // rescale of last round's weights since they were written
   unsigned long long hot;
 };
 
@@ -337,6 +346,24 @@ __device__ __forceinline__ void add_lo(uint32_t word, float wo, float (&acc)[16]
   for (int i = 0; i < 16; i += 2) {
     acc[i] = fmaf(we, x[i], acc[i]);
     acc[i + 1] = fmaf(wo, x[i + 1], acc[i + 1]);
+  }
+}
+
+// Adds the low planes loaded in the previous round (parity pr): the words of that round's hot
+// tokens, with that round's weights times the rescale applied since.
+template <int NVG, int NW>
+__device__ __forceinline__ void add_prev_lo(Smem<NVG, NW>& sm, WaveState<NVG>& st, int pr, int w,
+                                            int lane, float lo_scale) {
+  const int slot = lane >> 3;
+  const int vg_lane = ((lane & 7) * 16) / (kHeadDim / NVG);
+  const float sc = lo_scale * st.lo_f;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const int idx = 8 * kk + slot;
+    if (8 * kk < st.nlo && idx < st.nlo) {
+      const int T = sm.hot_list[pr][w][idx].x;
+      add_lo(st.lo_word[kk], sm.wbuf[pr][w][vg_lane][T] * sc, st.acc);
+    }
   }
 }
 
@@ -451,17 +478,13 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
       for (int i = 0; i < NVG; ++i) st.Csum[i] *= f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) st.acc[i] *= f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.lo_wt[i] *= f;
+      st.lo_f *= f;
     }
     st.M = gm;
   }
   // ---- last round's low planes
-  if (BITS == 4) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      if (st.lo_wt[kk] != 0.f) add_lo(st.lo_word[kk], st.lo_wt[kk], st.acc);
-  }
+  if (BITS == 4) add_prev_lo<NVG, NW>(sm, st, (rd + 1) & 1, w, lane, k.lo_scale);
+  const int pr = rd & 1;
 
   // ---- per token (every lane): weight, hot/cold, value scale/zero folds
   bool hot = false;
@@ -476,22 +499,22 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
       // Csum gathers p * z, plus p * 1.5 * s for a cold token (middle of its bucket)
       const float zc = (k.gated && !hot) ? fmaf(1.5f, f16_lo(sz), f16_hi(sz)) : f16_hi(sz);
       st.Csum[i] = fmaf(p, zc, st.Csum[i]);
-      sm.wbuf[w][i][lane] = fmaf(pw, f16_lo(sz), 0.f);   // kWScale * weight
+      sm.wbuf[pr][w][i][lane] = fmaf(pw, f16_lo(sz), 0.f);   // kWScale * weight
     }
     if (k.mask_row) k.mask_row[(size_t)(gA + half) * kGroup + hl] = hot ? 1 : 0;
   } else {
 #pragma unroll
-    for (int i = 0; i < NVG; ++i) sm.wbuf[w][i][lane] = 0.f;
+    for (int i = 0; i < NVG; ++i) sm.wbuf[pr][w][i][lane] = 0.f;
   }
   const unsigned long long hotmask = __ballot(hot);
   if (BITS == 4 && hot) {
     const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(hotmask >> 32),
                                               __builtin_amdgcn_mbcnt_lo((uint32_t)hotmask, 0u));
-    sm.hot_list[w][pos] = make_int2(lane, cur.pid);
+    sm.hot_list[pr][w][pos] = make_int2(lane, cur.pid);
   }
   wave_lds_sync();
 
-  // ---- low-plane loads of the hot tokens: the first 32 accumulate next round, any more now
+  // ---- low-plane loads of the hot tokens, added next round
   if (BITS == 4) {
     const int nhot = __popcll(hotmask);
     st.hot += nhot;
@@ -500,27 +523,21 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int idx = 8 * kk + slot;
-      if (kk < 4) st.lo_wt[kk] = 0.f;
       if (8 * kk < nhot && idx < nhot) {
-        const int2 e = sm.hot_list[w][idx];
-        const int T = e.x, t = T & 31;
-        const uint32_t word = gp<uint32_t>(page_at(r, e.y) + lay.vlo)[(t % P) * (kHeadDim / 16) + cbv];
-        const float wo = sm.wbuf[w][vg_lane][T] * k.lo_scale;
-        if (kk < 4) {
-          st.lo_word[kk] = word;
-          st.lo_wt[kk] = wo;
-        } else {
-          add_lo(word, wo, st.acc);
-        }
+        const int2 e = sm.hot_list[pr][w][idx];
+        const int t = e.x & 31;
+        st.lo_word[kk] = gp<uint32_t>(page_at(r, e.y) + lay.vlo)[(t % P) * (kHeadDim / 16) + cbv];
       }
     }
+    st.nlo = nhot;
+    st.lo_f = 1.f;
   }
 
   // ---- high plane (INT4) or codes (INT2): 8 tokens of the lane's group, in 4 token pairs
   {
     const int tb = half * 32 + (hl >> 3) * 8;
-    const float4 wa = *reinterpret_cast<const float4*>(&sm.wbuf[w][vg_lane][tb]);
-    const float4 wb = *reinterpret_cast<const float4*>(&sm.wbuf[w][vg_lane][tb + 4]);
+    const float4 wa = *reinterpret_cast<const float4*>(&sm.wbuf[pr][w][vg_lane][tb]);
+    const float4 wb = *reinterpret_cast<const float4*>(&sm.wbuf[pr][w][vg_lane][tb + 4]);
     const half2v p0 = pack_h2(wa.x, wa.y);
     const half2v p1 = pack_h2(wa.z, wa.w);
     const half2v p2 = pack_h2(wb.x, wb.y);
@@ -642,7 +659,9 @@ __global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(Deco
 #pragma unroll
   for (int i = 0; i < 16; ++i) st.acc[i] = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { st.lo_word[i] = 0u; st.lo_wt[i] = 0.f; }
+  for (int i = 0; i < 8; ++i) st.lo_word[i] = 0u;
+  st.nlo = 0;
+  st.lo_f = 1.f;
 
   const int cbv = lane & 7, tq8 = lane >> 3;
   const int rounds = (ge - gs + 2 * NW - 1) / (2 * NW);
@@ -661,11 +680,7 @@ __global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(Deco
     if (rd + 1 < rounds) round_body<BITS, NVG, P, NW>(sm, st, rb, ra, nid, r, offs, k, rd + 1);
   }
   // Low planes of the last round.
-  if (BITS == 4) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      if (st.lo_wt[kk] != 0.f) add_lo(st.lo_word[kk], st.lo_wt[kk], st.acc);
-  }
+  if (BITS == 4 && rounds > 0) add_prev_lo<NVG, NW>(sm, st, (rounds - 1) & 1, w, lane, k.lo_scale);
 
   // Exact tail tokens (last split only), in chunks of 32, distributed over the waves.
   if (do_tail) {
@@ -708,8 +723,6 @@ __global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(Deco
           for (int i = 0; i < NVG; ++i) st.Csum[i] *= f;
 #pragma unroll
           for (int i = 0; i < 16; ++i) st.acc[i] *= f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) st.lo_wt[i] *= f;
         }
         st.M = gmx;
       }
@@ -717,7 +730,7 @@ __global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(Deco
         const float p = (ch * kGroup + lane < n_tail) ? fexp2(s2 - st.M) : 0.f;
         st.Lsum += p;
         // odd-channel weight in offset units: (p / VS) * kWScale / 16; even channels 4x that
-        sm.wbuf[w][0][lane] = p * (kWScale / 16.f / VS);
+        sm.wbuf[0][w][0][lane] = p * (kWScale / 16.f / VS);
       }
       wave_lds_sync();
       for (int j = 0; j < 4; ++j) {
@@ -728,7 +741,7 @@ __global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(Deco
         const LKV_GLOBAL u32x4* vp = reinterpret_cast<const LKV_GLOBAL u32x4*>(tail_v + row * kHeadDim + cbv * 16);
         const u32x4 v0 = vp[0], v1 = vp[1];
         const uint32_t vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const float wt = sm.wbuf[w][0][t];
+        const float wt = sm.wbuf[0][w][0][t];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           // exact values, offset-free: even channels weigh 4x the odd ones (f = 1/4 vs 1/16)
