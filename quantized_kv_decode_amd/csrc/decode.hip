@@ -24,10 +24,11 @@
 // tokens are loaded in that round and accumulated in the next.
 //
 // Arithmetic:
-//  - keys: a 2- or 4-bit code in the low bits of an fp8 (E4M3) byte converts exactly to
-//    code * u (u = the value of byte 0x01), since E4M3's subnormals and first binade are evenly
-//    spaced up to 15u; one masked word gives four codes as floats in two packed conversions.
-//    The score is an fp32 FMA chain, so the hot/cold test sees fp32-accurate scores.
+//  - keys: a 4-bit code in the low bits of an fp8 (E4M3) byte converts exactly to code * u
+//    (u = the value of byte 0x01), since E4M3's subnormals and first binade are evenly spaced
+//    up to 15u; a 2-bit code in the low bits of an fp4 (E2M1) nibble converts exactly to
+//    code / 2. One conversion gives two codes as floats. The score is an fp32 FMA chain, so
+//    the hot/cold test sees fp32-accurate scores.
 //  - values (INT4 high plane, INT2 codes): two tokens' words are interleaved with one byte
 //    permute so each 16-bit half holds one token's channels; a code moved to mantissa bits 6..9
 //    and OR-ed with the exponent of 1.0 is the fp16 number 1 + c/16 or 1 + c/4, and one
@@ -77,9 +78,6 @@ __device__ __forceinline__ float2v cvt2(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
 }
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ half2v pack_h2(float a, float b) {
-  return __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(a, b));
-}
 __device__ __forceinline__ float dot2(half2v a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(a, __builtin_bit_cast(half2v, b), c, false);
 }
@@ -128,19 +126,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// 16 two-bit codes of a word (channel i at bits 2i) as floats: code * u * (i odd ? 4 : 1).
+// Byte SEL of w as two fp4 (E2M1) numbers, low nibble first, times 2. A 2-bit code in the low
+// bits of a nibble (sign and high exponent bit clear) is the E2M1 number code / 2: 0, 0.5
+// (the subnormal), 1, 1.5.
+template <int SEL>
+__device__ __forceinline__ float2v fp4x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 2.0f, SEL);
+}
+
+// 16 two-bit codes of a word (channel i at bits 2i) as floats equal to the codes.
 __device__ __forceinline__ void unpack16(uint32_t w, float (&x)[16]) {
-  const uint32_t m0 = w & 0x03030303u, m1 = w & 0x0C0C0C0Cu;
-  const uint32_t w4 = w >> 4;
-  const uint32_t m2 = w4 & 0x03030303u, m3 = w4 & 0x0C0C0C0Cu;
-  float2v a = cvt2<false>(m0), b = cvt2<true>(m0);   // channels 0,4 | 8,12
-  float2v c = cvt2<false>(m1), d = cvt2<true>(m1);   // 1,5 | 9,13 (x4)
-  float2v e = cvt2<false>(m2), f = cvt2<true>(m2);   // 2,6 | 10,14
-  float2v g = cvt2<false>(m3), h = cvt2<true>(m3);   // 3,7 | 11,15 (x4)
-  x[0] = a.x; x[4] = a.y; x[8] = b.x; x[12] = b.y;
-  x[1] = c.x; x[5] = c.y; x[9] = d.x; x[13] = d.y;
-  x[2] = e.x; x[6] = e.y; x[10] = f.x; x[14] = f.y;
-  x[3] = g.x; x[7] = g.y; x[11] = h.x; x[15] = h.y;
+  const uint32_t e = w & 0x33333333u;          // nibble j: code of channel 2j
+  const uint32_t o = (w >> 2) & 0x33333333u;   // nibble j: code of channel 2j + 1
+  const float2v e0 = fp4x2<0>(e), e1 = fp4x2<1>(e), e2 = fp4x2<2>(e), e3 = fp4x2<3>(e);
+  const float2v o0 = fp4x2<0>(o), o1 = fp4x2<1>(o), o2 = fp4x2<2>(o), o3 = fp4x2<3>(o);
+  x[0] = e0.x; x[2] = e0.y; x[4] = e1.x; x[6] = e1.y; x[8] = e2.x; x[10] = e2.y; x[12] = e3.x; x[14] = e3.y;
+  x[1] = o0.x; x[3] = o0.y; x[5] = o1.x; x[7] = o1.y; x[9] = o2.x; x[11] = o2.y; x[13] = o3.x; x[15] = o3.y;
 }
 
 // 8 four-bit codes of a word (channel i at bits 4i) as floats: code * u.
@@ -193,7 +194,8 @@ struct Smem {
   // Per-wave value weights [round parity][wave][value group][token of pair] and hot tokens
   // (token of pair, page id); the low planes of a round are added in the next one, which reads
   // that round's copies.
-  alignas(16) float wbuf[2][NW][NVG][64];
+  alignas(16) _Float16 wbuf[2][NW][NVG][64];
+  float tail_w[NW][kGroup];               // exact tail weights
   int2 hot_list[2][NW][64];
   float gmax[2][NW][2];
   float fin_acc[NW][kHeadDim];
@@ -328,7 +330,7 @@ struct WaveState {
 };
 
 struct RoundConst {
-  float scale2, log2tau, u, lo_scale;   // lo_scale = 1 / (kWScale * u)
+  float scale2, log2tau, u, lo_scale;   // lo_scale = 4 / kWScale
   bool gated;
   int w, lane, gs, ge;
   uint8_t* mask_row;
@@ -336,12 +338,12 @@ struct RoundConst {
 };
 
 // Adds a low-plane word (16 channels, 2-bit codes) with odd-channel weight wo: a low code is a
-// quarter of a value code step, and unpack16's scale (u, and 4u on odd channels) and the offset
-// units (f = 1/4 even, 1/16 odd) fold into wo and 16 * wo.
+// quarter of a high-plane code step, and the offset units (f = 1/4 even, 1/16 odd) make the
+// even-channel weight 4 * wo.
 __device__ __forceinline__ void add_lo(uint32_t word, float wo, float (&acc)[16]) {
   float x[16];
   unpack16(word, x);
-  const float we = 16.f * wo;
+  const float we = 4.f * wo;
 #pragma unroll
   for (int i = 0; i < 16; i += 2) {
     acc[i] = fmaf(we, x[i], acc[i]);
@@ -362,7 +364,7 @@ __device__ __forceinline__ void add_prev_lo(Smem<NVG, NW>& sm, WaveState<NVG>& s
     const int idx = 8 * kk + slot;
     if (8 * kk < st.nlo && idx < st.nlo) {
       const int T = sm.hot_list[pr][w][idx].x;
-      add_lo(st.lo_word[kk], sm.wbuf[pr][w][vg_lane][T] * sc, st.acc);
+      add_lo(st.lo_word[kk], (float)sm.wbuf[pr][w][vg_lane][T] * sc, st.acc);
     }
   }
 }
@@ -408,17 +410,16 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   // its weights 0): then every path through the round consumes the same loads.
   float s2;
   {
-    float qs[KCH], ke = 0.f, ko = 0.f;
+    float qs[KCH], ke = 0.f;
     const uint32_t* kszw = reinterpret_cast<const uint32_t*>(cur.ksz);
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const uint32_t sz = kszw[i];
       qs[i] = fmaf(qv[i], f16_lo(sz), 0.f);      // fp16 operand: one v_fma_mix_f32
-      if (BITS == 2 && (i & 1)) ko = fmaf(qv[i], f16_hi(sz), ko);
-      else ke = fmaf(qv[i], f16_hi(sz), ke);
+      ke = fmaf(qv[i], f16_hi(sz), ke);
     }
-    // qv carries 1/u (and 1/4 on odd INT2 channels): kappa = sum_c q_c * z_c
-    const float kappa = (BITS == 2 ? fmaf(4.f, ko, ke) : ke) * k.u;
+    // kappa = sum_c q_c * z_c (the INT4 operand carries 1/u)
+    const float kappa = BITS == 4 ? ke * k.u : ke;
     const uint32_t* kw = reinterpret_cast<const uint32_t*>(cur.kc);
     float part[KTOK];
 #pragma unroll
@@ -499,12 +500,15 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
       // Csum gathers p * z, plus p * 1.5 * s for a cold token (middle of its bucket)
       const float zc = (k.gated && !hot) ? fmaf(1.5f, f16_lo(sz), f16_hi(sz)) : f16_hi(sz);
       st.Csum[i] = fmaf(p, zc, st.Csum[i]);
-      sm.wbuf[pr][w][i][lane] = fmaf(pw, f16_lo(sz), 0.f);   // kWScale * weight
+      // kWScale * weight, rounded to nearest fp16: the value codes and the offset W both use
+      // this rounded weight, and its error is unbiased (a truncated weight would bias the code
+      // sum, which the zero term largely cancels in the output)
+      sm.wbuf[pr][w][i][lane] = (_Float16)fmaf(pw, f16_lo(sz), 0.f);
     }
     if (k.mask_row) k.mask_row[(size_t)(gA + half) * kGroup + hl] = hot ? 1 : 0;
   } else {
 #pragma unroll
-    for (int i = 0; i < NVG; ++i) sm.wbuf[pr][w][i][lane] = 0.f;
+    for (int i = 0; i < NVG; ++i) sm.wbuf[pr][w][i][lane] = (_Float16)0.f;
   }
   const unsigned long long hotmask = __ballot(hot);
   if (BITS == 4 && hot) {
@@ -536,12 +540,11 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   // ---- high plane (INT4) or codes (INT2): 8 tokens of the lane's group, in 4 token pairs
   {
     const int tb = half * 32 + (hl >> 3) * 8;
-    const float4 wa = *reinterpret_cast<const float4*>(&sm.wbuf[pr][w][vg_lane][tb]);
-    const float4 wb = *reinterpret_cast<const float4*>(&sm.wbuf[pr][w][vg_lane][tb + 4]);
-    const half2v p0 = pack_h2(wa.x, wa.y);
-    const half2v p1 = pack_h2(wa.z, wa.w);
-    const half2v p2 = pack_h2(wb.x, wb.y);
-    const half2v p3 = pack_h2(wb.z, wb.w);
+    const uint4 wq = *reinterpret_cast<const uint4*>(&sm.wbuf[pr][w][vg_lane][tb]);
+    const half2v p0 = __builtin_bit_cast(half2v, wq.x);   // tokens tb, tb + 1
+    const half2v p1 = __builtin_bit_cast(half2v, wq.y);
+    const half2v p2 = __builtin_bit_cast(half2v, wq.z);
+    const half2v p3 = __builtin_bit_cast(half2v, wq.w);
     const uint32_t ones = k.mk.one;
     st.W = dot2(p0, ones, st.W);
     st.W = dot2(p1, ones, st.W);
@@ -597,8 +600,9 @@ __global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(Deco
     const uint16_t qb = c.q[((size_t)b * H + h) * kHeadDim + tid];
     const float q = __uint_as_float((uint32_t)qb << 16);
     sm.q[tid] = q;
-    // key operand: q / u, and q / (4u) on odd INT2 channels (their codes sit two bits up)
-    sm.qv[tid] = (BITS == 2 && (tid & 1)) ? q * 0.25f * inv_u : q * inv_u;
+    // key operand: q itself for INT2 codes (converted to their values), q / u for INT4 codes
+    // (converted to code * u)
+    sm.qv[tid] = BITS == 2 ? q : q * inv_u;
   }
   if (tid == 0) sm.cnt_hot = 0;
 
@@ -638,7 +642,7 @@ __global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(Deco
   k.scale2 = c.sm_scale * kLog2e;
   k.log2tau = c.tau > 0.f ? log2f(c.tau) : -INFINITY;
   k.u = u;
-  k.lo_scale = inv_u * (1.f / kWScale);
+  k.lo_scale = 4.f / kWScale;
   k.w = w;
   k.lane = lane;
   k.gs = gs;
@@ -730,7 +734,7 @@ __global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(Deco
         const float p = (ch * kGroup + lane < n_tail) ? fexp2(s2 - st.M) : 0.f;
         st.Lsum += p;
         // odd-channel weight in offset units: (p / VS) * kWScale / 16; even channels 4x that
-        sm.wbuf[0][w][0][lane] = p * (kWScale / 16.f / VS);
+        sm.tail_w[w][lane] = p * (kWScale / 16.f / VS);
       }
       wave_lds_sync();
       for (int j = 0; j < 4; ++j) {
@@ -741,7 +745,7 @@ __global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(Deco
         const LKV_GLOBAL u32x4* vp = reinterpret_cast<const LKV_GLOBAL u32x4*>(tail_v + row * kHeadDim + cbv * 16);
         const u32x4 v0 = vp[0], v1 = vp[1];
         const uint32_t vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const float wt = sm.wbuf[0][w][0][t];
+        const float wt = sm.tail_w[w][t];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           // exact values, offset-free: even channels weigh 4x the odd ones (f = 1/4 vs 1/16)
