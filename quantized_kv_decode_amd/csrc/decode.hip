@@ -18,10 +18,11 @@
 // maximum, so the hot/cold decisions are exactly those of streaming the split group by group.
 // Each wave keeps its own online-softmax state; the waves merge at the end.
 //
-// Latency hiding: every data-independent load of a wave's next two groups (key codes and
-// scales, value high plane or INT2 codes, value scales) is issued one round ahead into a second
-// set of registers (the round loop alternates the two sets); the low planes of a round's hot
-// tokens are loaded in that round and accumulated in the next.
+// Latency hiding: each part of a wave's next two groups (key codes and scales, value scales,
+// value high plane or INT2 codes) is loaded right after this round's last use of the same
+// registers, so it has about a round to arrive; page ids are read a round before the loads
+// that use them; the low planes of a round's hot tokens are loaded in that round and added in
+// the next.
 //
 // Arithmetic:
 //  - keys: a 4-bit code in the low bits of an fp8 (E4M3) byte converts exactly to code * u
@@ -196,14 +197,19 @@ struct Smem {
   // that round's copies.
   alignas(16) _Float16 wbuf[2][NW][NVG][64];
   float tail_w[NW][kGroup];               // exact tail weights
-  int2 hot_list[2][NW][64];
+  // Hot tokens of a round, compacted: address of the token's low-plane row, and its value
+  // weights / 4 as fp16 (a low code is a quarter of a high-plane step), with a zero after the
+  // last so that tokens are read in pairs.
+  unsigned long long hot_addr[2][NW][64];
+  alignas(4) _Float16 hot_w[2][NW][NVG][66];
   float gmax[2][NW][2];
   float fin_acc[NW][kHeadDim];
   float fin_M[NW], fin_L[NW], fin_C[NW][NVG];
   unsigned long long cnt_hot;
 };
 
-// Per-lane registers of one pair of groups, loaded one round ahead.
+// Per-lane registers of one pair of groups. Each part is reloaded for the next round right
+// after this round's last use of it, so one set of registers keeps a round of loads in flight.
 template <int BITS, int NVG>
 struct PairRegs {
   static constexpr int KCW = BITS == 4 ? 4 : 2;   // 16-byte loads of key code words
@@ -212,7 +218,6 @@ struct PairRegs {
   u32x4 ksz[KSW];
   u32x4 vc[2];
   uint32_t vsz[NVG];
-  int pid;          // page holding the lane's token (its low plane is read from there)
 };
 
 struct RowCtx {
@@ -278,39 +283,41 @@ __device__ __forceinline__ LaneOffs lane_offsets(const Layout& lay, int lane) {
   return o;
 }
 
-template <int BITS, int NVG>
-__device__ __forceinline__ void load_pair(PairRegs<BITS, NVG>& g, gbytes tok_page, gbytes first_page,
-                                          const LaneOffs& o) {
-  {
-    const LKV_GLOBAL u32x4* p = gp<u32x4>(tok_page + o.kc);
-#pragma unroll
-    for (int i = 0; i < PairRegs<BITS, NVG>::KCW; ++i) g.kc[i] = p[i];
-  }
-  {
-    const LKV_GLOBAL u32x4* p = gp<u32x4>(first_page + o.ksz);
-#pragma unroll
-    for (int i = 0; i < PairRegs<BITS, NVG>::KSW; ++i) g.ksz[i] = p[i];
-  }
-  {
-    const LKV_GLOBAL u32x4* p = gp<u32x4>(tok_page + o.vc);
-    g.vc[0] = p[0];
-    g.vc[1] = p[1];
-  }
-  {
-    const LKV_GLOBAL uint32_t* p = gp<uint32_t>(tok_page + o.vsz);
-#pragma unroll
-    for (int i = 0; i < NVG; ++i) g.vsz[i] = p[i];
-  }
+// Page addresses of a lane's loads for one pair of groups.
+struct PairPages {
+  gbytes tok, first;
+  int tok_pid;
+};
+
+template <int P>
+__device__ __forceinline__ PairPages pair_pages(const RowCtx& r, const LaneIds& id) {
+  PairPages pp;
+  pp.tok_pid = checked_page(r, id.tok);
+  pp.tok = page_at(r, pp.tok_pid);
+  pp.first = P == kGroup ? pp.tok : page_at(r, checked_page(r, id.first));
+  return pp;
 }
 
-// Issues the loads of the pair whose lane page ids are `id`.
-template <int BITS, int NVG, int P>
-__device__ __forceinline__ void fetch_pair(PairRegs<BITS, NVG>& g, const RowCtx& r, const LaneIds& id,
-                                           const LaneOffs& o) {
-  const int tp = checked_page(r, id.tok);
-  const int fp = P == kGroup ? tp : checked_page(r, id.first);
-  g.pid = tp;
-  load_pair<BITS, NVG>(g, page_at(r, tp), page_at(r, fp), o);
+template <int BITS, int NVG>
+__device__ __forceinline__ void load_keys(PairRegs<BITS, NVG>& g, const PairPages& pp, const LaneOffs& o) {
+  const LKV_GLOBAL u32x4* kc = gp<u32x4>(pp.tok + o.kc);
+#pragma unroll
+  for (int i = 0; i < PairRegs<BITS, NVG>::KCW; ++i) g.kc[i] = kc[i];
+  const LKV_GLOBAL u32x4* ksz = gp<u32x4>(pp.first + o.ksz);
+#pragma unroll
+  for (int i = 0; i < PairRegs<BITS, NVG>::KSW; ++i) g.ksz[i] = ksz[i];
+}
+template <int BITS, int NVG>
+__device__ __forceinline__ void load_vsz(PairRegs<BITS, NVG>& g, const PairPages& pp, const LaneOffs& o) {
+  const LKV_GLOBAL uint32_t* p = gp<uint32_t>(pp.tok + o.vsz);
+#pragma unroll
+  for (int i = 0; i < NVG; ++i) g.vsz[i] = p[i];
+}
+template <int BITS, int NVG>
+__device__ __forceinline__ void load_vc(PairRegs<BITS, NVG>& g, const PairPages& pp, const LaneOffs& o) {
+  const LKV_GLOBAL u32x4* p = gp<u32x4>(pp.tok + o.vc);
+  g.vc[0] = p[0];
+  g.vc[1] = p[1];
 }
 
 // Softmax and value accumulation state of one wave.
@@ -323,57 +330,46 @@ struct WaveState {
   // (odd i), and W collects the w'; low planes and exact tail values are added without the
   // offset. True weighted sum of channel i = (acc[i] - W) / (f_i * kWScale).
   float acc[16];
-  uint32_t lo_word[8];           // low planes of last round's hot tokens
+  uint32_t lo_word[8];           // low planes of last round's hot tokens, two per lane and pass
   int nlo;                       // last round's hot count
-  float lo_f;                    // rescale of last round's weights since they were written
   unsigned long long hot;
 };
 
 struct RoundConst {
-  float scale2, log2tau, u, lo_scale;   // lo_scale = 4 / kWScale
+  float scale2, log2tau, u;
   bool gated;
   int w, lane, gs, ge;
   uint8_t* mask_row;
   Masks mk;
 };
 
-// Adds a low-plane word (16 channels, 2-bit codes) with odd-channel weight wo: a low code is a
-// quarter of a high-plane code step, and the offset units (f = 1/4 even, 1/16 odd) make the
-// even-channel weight 4 * wo.
-__device__ __forceinline__ void add_lo(uint32_t word, float wo, float (&acc)[16]) {
-  float x[16];
-  unpack16(word, x);
-  const float we = 4.f * wo;
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    acc[i] = fmaf(we, x[i], acc[i]);
-    acc[i + 1] = fmaf(wo, x[i + 1], acc[i + 1]);
-  }
-}
-
-// Adds the low planes loaded in the previous round (parity pr): the words of that round's hot
-// tokens, with that round's weights times the rescale applied since.
+// Adds the low planes loaded in the previous round (parity pr), before this round changes the
+// wave's maximum, so that round's weights still apply. Pass j covers hot tokens 16j .. 16j+15:
+// lane (slot, cbv) holds channels 16*cbv.. of tokens 16j + 2*slot and 16j + 2*slot + 1, which
+// enter like a high-plane token pair (offset units, weights / 4).
 template <int NVG, int NW>
 __device__ __forceinline__ void add_prev_lo(Smem<NVG, NW>& sm, WaveState<NVG>& st, int pr, int w,
-                                            int lane, float lo_scale) {
+                                            int lane, const Masks& mk) {
   const int slot = lane >> 3;
   const int vg_lane = ((lane & 7) * 16) / (kHeadDim / NVG);
-  const float sc = lo_scale * st.lo_f;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const int idx = 8 * kk + slot;
-    if (8 * kk < st.nlo && idx < st.nlo) {
-      const int T = sm.hot_list[pr][w][idx].x;
-      add_lo(st.lo_word[kk], (float)sm.wbuf[pr][w][vg_lane][T] * sc, st.acc);
+  for (int j = 0; j < 4; ++j) {
+    if (16 * j < st.nlo) {
+      const int idx = 16 * j + 2 * slot;
+      uint32_t wpair = *reinterpret_cast<const uint32_t*>(&sm.hot_w[pr][w][vg_lane][idx]);
+      if (idx >= st.nlo) wpair = 0u;
+      const half2v wp = __builtin_bit_cast(half2v, wpair);
+      st.W = dot2(wp, mk.one, st.W);
+      dot2_pair(st.lo_word[2 * j], st.lo_word[2 * j + 1], wp, mk, st.acc);
     }
   }
 }
 
 template <int BITS, int NVG, int P, int NW>
 __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st,
-                                           const PairRegs<BITS, NVG>& cur, PairRegs<BITS, NVG>& nxt,
-                                           LaneIds& nid, const RowCtx& r, const LaneOffs& lo,
-                                           const RoundConst& k, int rd) {
+                                           PairRegs<BITS, NVG>& cur, int& pid_cur, LaneIds& nid,
+                                           const RowCtx& r, const LaneOffs& lo, const RoundConst& k,
+                                           int rd) {
   constexpr int KCH = 32 / BITS;
   constexpr int NCB = kHeadDim / KCH;
   constexpr int KTOK = NCB;
@@ -386,15 +382,13 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   const bool active = gA < k.ge;
   const bool validB = gA + 1 < k.ge;
   const bool my_valid = half ? validB : active;
-  {
-    // The next pair's loads (page ids read last round) and the page ids of the pair after it.
-    // Both are issued on every round, also when the wave has no next pair (then it re-reads
-    // the split's last group, which is cached): with a fixed number of loads per round the
-    // wait before this round's data leaves the next round's loads in flight.
-    const LaneIds id = nid;
-    nid = load_ids<P>(r, gA + 4 * NW, k.ge, lane);
-    fetch_pair<BITS, NVG, P>(nxt, r, id, lo);
-  }
+  // The next pair's pages (ids read last round); the ids of the pair after it. All loads are
+  // issued on every round, also when the wave has no next pair (then it re-reads the split's
+  // last group, which is cached): with a fixed number of loads per round every wait leaves
+  // the younger loads in flight.
+  const PairPages np = pair_pages<P>(r, nid);
+  nid = load_ids<P>(r, gA + 4 * NW, k.ge, lane);
+
   float qv[KCH];   // the lane's key operand (q / u), re-read from LDS to spare registers
   {
     const float4* qp = reinterpret_cast<const float4*>(&sm.qv[cb * KCH]);
@@ -442,6 +436,7 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
 #pragma unroll
     for (int j = 0; j < KTOK; j += 4)
       *reinterpret_cast<float4*>(red + j) = make_float4(part[j], part[j + 1], part[j + 2], part[j + 3]);
+    load_keys<BITS, NVG>(cur, np, lo);   // next round's keys
     wave_lds_sync();
     float raw = 0.f;
 #pragma unroll
@@ -468,6 +463,9 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   const float mpreB = dmax(mpreA, gmB);
   st.m_run = mall;
 
+  // ---- last round's low planes, before this round can move the wave's maximum
+  if (BITS == 4) add_prev_lo<NVG, NW>(sm, st, (rd + 1) & 1, w, lane, k.mk);
+
   // ---- online softmax: rescale only when the wave's maximum grows
   const float gm = dmax(gmA, gmB);
   if (gm > st.M) {
@@ -479,16 +477,14 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
       for (int i = 0; i < NVG; ++i) st.Csum[i] *= f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) st.acc[i] *= f;
-      st.lo_f *= f;
     }
     st.M = gm;
   }
-  // ---- last round's low planes
-  if (BITS == 4) add_prev_lo<NVG, NW>(sm, st, (rd + 1) & 1, w, lane, k.lo_scale);
   const int pr = rd & 1;
 
   // ---- per token (every lane): weight, hot/cold, value scale/zero folds
   bool hot = false;
+  _Float16 wv[NVG];   // the token's value weights (kWScale * p * s, fp16)
   if (my_valid) {
     const float p = fexp2(s2 - st.M);
     hot = !(k.gated && (s2 - (half ? mpreB : mpreA)) < k.log2tau);
@@ -503,38 +499,48 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
       // kWScale * weight, rounded to nearest fp16: the value codes and the offset W both use
       // this rounded weight, and its error is unbiased (a truncated weight would bias the code
       // sum, which the zero term largely cancels in the output)
-      sm.wbuf[pr][w][i][lane] = (_Float16)fmaf(pw, f16_lo(sz), 0.f);
+      wv[i] = (_Float16)fmaf(pw, f16_lo(sz), 0.f);
+      sm.wbuf[pr][w][i][lane] = wv[i];
     }
     if (k.mask_row) k.mask_row[(size_t)(gA + half) * kGroup + hl] = hot ? 1 : 0;
   } else {
 #pragma unroll
-    for (int i = 0; i < NVG; ++i) sm.wbuf[pr][w][i][lane] = (_Float16)0.f;
+    for (int i = 0; i < NVG; ++i) {
+      wv[i] = (_Float16)0.f;
+      sm.wbuf[pr][w][i][lane] = wv[i];
+    }
   }
+  load_vsz<BITS, NVG>(cur, np, lo);   // next round's value scales
   const unsigned long long hotmask = __ballot(hot);
+  const int nhot = __popcll(hotmask);
   if (BITS == 4 && hot) {
     const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(hotmask >> 32),
                                               __builtin_amdgcn_mbcnt_lo((uint32_t)hotmask, 0u));
-    sm.hot_list[pr][w][pos] = make_int2(lane, cur.pid);
+    constexpr Layout lay = head_layout(BITS, P, kHeadDim, NVG);
+    sm.hot_addr[pr][w][pos] = (unsigned long long)(page_at(r, pid_cur) + lay.vlo + (hl % P) * (kHeadDim / 4));
+#pragma unroll
+    for (int i = 0; i < NVG; ++i) {
+      sm.hot_w[pr][w][i][pos] = wv[i] * (_Float16)0.25f;
+      if (pos == nhot - 1) sm.hot_w[pr][w][i][pos + 1] = (_Float16)0.f;
+    }
   }
   wave_lds_sync();
 
-  // ---- low-plane loads of the hot tokens, added next round
+  // ---- low-plane loads of the hot tokens, two per lane and pass, added next round
   if (BITS == 4) {
-    const int nhot = __popcll(hotmask);
     st.hot += nhot;
     const int slot = lane >> 3;
-    constexpr Layout lay = head_layout(BITS, P, kHeadDim, NVG);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int idx = 8 * kk + slot;
-      if (8 * kk < nhot && idx < nhot) {
-        const int2 e = sm.hot_list[pr][w][idx];
-        const int t = e.x & 31;
-        st.lo_word[kk] = gp<uint32_t>(page_at(r, e.y) + lay.vlo)[(t % P) * (kHeadDim / 16) + cbv];
+    for (int j = 0; j < 4; ++j) {
+      if (16 * j < nhot) {
+        const int idx = 16 * j + 2 * slot;
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (idx + e < nhot)
+            st.lo_word[2 * j + e] = gp<uint32_t>((gbytes)sm.hot_addr[pr][w][idx + e])[cbv];
       }
     }
     st.nlo = nhot;
-    st.lo_f = 1.f;
   }
 
   // ---- high plane (INT4) or codes (INT2): 8 tokens of the lane's group, in 4 token pairs
@@ -555,6 +561,8 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
     dot2_pair(cur.vc[1].x, cur.vc[1].y, p2, k.mk, st.acc);
     dot2_pair(cur.vc[1].z, cur.vc[1].w, p3, k.mk, st.acc);
   }
+  load_vc<BITS, NVG>(cur, np, lo);   // next round's value codes
+  pid_cur = np.tok_pid;
   wave_lds_sync();
 }
 
@@ -642,7 +650,6 @@ __global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(Deco
   k.scale2 = c.sm_scale * kLog2e;
   k.log2tau = c.tau > 0.f ? log2f(c.tau) : -INFINITY;
   k.u = u;
-  k.lo_scale = 4.f / kWScale;
   k.w = w;
   k.lane = lane;
   k.gs = gs;
@@ -665,26 +672,29 @@ __global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(Deco
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.lo_word[i] = 0u;
   st.nlo = 0;
-  st.lo_f = 1.f;
 
   const int cbv = lane & 7, tq8 = lane >> 3;
   const int rounds = (ge - gs + 2 * NW - 1) / (2 * NW);
   const LaneOffs offs = lane_offsets<BITS, NVG, P>(lay, lane);
-  PairRegs<BITS, NVG> ra, rb;
-  LaneIds nid{0, 0};   // page ids of the pair after the one in flight
+  PairRegs<BITS, NVG> regs;
+  LaneIds nid{0, 0};   // page ids of the next round's pair
+  int pid_cur = 0;     // page holding the lane's token this round
   if (rounds > 0) {
+    // the next round's ids go out before this round's data, as inside the loop
     const int gA = gs + 2 * w;
-    fetch_pair<BITS, NVG, P>(ra, r, load_ids<P>(r, gA, ge, lane), offs);
+    const LaneIds id0 = load_ids<P>(r, gA, ge, lane);
     nid = load_ids<P>(r, gA + 2 * NW, ge, lane);
+    const PairPages pp = pair_pages<P>(r, id0);
+    load_keys<BITS, NVG>(regs, pp, offs);
+    load_vsz<BITS, NVG>(regs, pp, offs);
+    load_vc<BITS, NVG>(regs, pp, offs);
+    pid_cur = pp.tok_pid;
   }
   __syncthreads();
 
-  for (int rd = 0; rd < rounds; rd += 2) {
-    round_body<BITS, NVG, P, NW>(sm, st, ra, rb, nid, r, offs, k, rd);
-    if (rd + 1 < rounds) round_body<BITS, NVG, P, NW>(sm, st, rb, ra, nid, r, offs, k, rd + 1);
-  }
+  for (int rd = 0; rd < rounds; ++rd) round_body<BITS, NVG, P, NW>(sm, st, regs, pid_cur, nid, r, offs, k, rd);
   // Low planes of the last round.
-  if (BITS == 4 && rounds > 0) add_prev_lo<NVG, NW>(sm, st, (rounds - 1) & 1, w, lane, k.lo_scale);
+  if (BITS == 4 && rounds > 0) add_prev_lo<NVG, NW>(sm, st, (rounds - 1) & 1, w, lane, k.mk);
 
   // Exact tail tokens (last split only), in chunks of 32, distributed over the waves.
   if (do_tail) {
