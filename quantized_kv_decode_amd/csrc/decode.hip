@@ -571,17 +571,10 @@ struct DecodeParams {
   DecodeCall c;
 };
 
-#ifndef LOOPKV_WAVES_PER_SIMD
-#define LOOPKV_WAVES_PER_SIMD 3
-#endif
-#if LOOPKV_WAVES_PER_SIMD > 0
-#define LKV_OCCUPANCY __attribute__((amdgpu_waves_per_eu(LOOPKV_WAVES_PER_SIMD, LOOPKV_WAVES_PER_SIMD)))
-#else
-#define LKV_OCCUPANCY
-#endif
 
 template <int BITS, int NVG, int P, int NW, int RB>
-__global__ __launch_bounds__(64 * NW * RB) LKV_OCCUPANCY void decode_kernel(DecodeParams prm) {
+__global__ __launch_bounds__(64 * NW * RB) __attribute__((amdgpu_waves_per_eu(NW, NW)))
+void decode_kernel(DecodeParams prm) {
   const Geom& g = prm.g;
   const DecodeCall& c = prm.c;
   constexpr int KCH = 32 / BITS;
@@ -851,17 +844,21 @@ __global__ __launch_bounds__(kHeadDim) void merge_kernel(Geom g, DecodeCall c) {
   c.out[row * kHeadDim + tid] = den > 0.f ? num / den : 0.f;
 }
 
-// Waves per workgroup, and the waves per SIMD the register allocation targets (0: compiler's
-// choice). Four (request, head) rows per CU keep a 1024-row launch in one generation.
-#ifndef LOOPKV_NW
-#define LOOPKV_NW 3
+// Waves per (request, head) row, which is also the waves per SIMD the register allocation
+// targets: with four rows per workgroup, one workgroup fills a CU. 2-bit cells fit 128 VGPRs
+// (four waves per SIMD); 4-bit cells need more and run three.
+#ifndef LOOPKV_NW2
+#define LOOPKV_NW2 4
 #endif
-constexpr int kNW = LOOPKV_NW;
+#ifndef LOOPKV_NW4
+#define LOOPKV_NW4 3
+#endif
 
 template <int BITS, int P, int RB>
 hipError_t launch_bpr(const Geom& g, const DecodeCall& c, hipStream_t stream) {
   DecodeParams prm{g, c};
   const dim3 grid((unsigned)c.n_split, (unsigned)(g.H / RB), (unsigned)c.batch);
+  constexpr int kNW = BITS == 2 ? LOOPKV_NW2 : LOOPKV_NW4;
   const unsigned threads = 64 * kNW * RB;
   switch (g.nvg) {
     case 1: decode_kernel<BITS, 1, P, kNW, RB><<<grid, threads, 0, stream>>>(prm); break;
