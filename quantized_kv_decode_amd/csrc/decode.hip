@@ -31,8 +31,8 @@
 //    code / 2. One conversion gives two codes as floats. The score is an fp32 FMA chain, so
 //    the hot/cold test sees fp32-accurate scores.
 //  - values (INT4 high plane, INT2 codes): two tokens' words are interleaved with one byte
-//    permute so each 16-bit half holds one token's channels; a code moved to mantissa bits 6..9
-//    and OR-ed with the exponent of 1.0 is the fp16 number 1 + c/16 or 1 + c/4, and one
+//    permute so each 16-bit half holds one token's channels; a code moved to mantissa bits 4..9
+//    and OR-ed with the exponent of 1.0 is the fp16 number 1 + c/64, 1 + c/16 or 1 + c/4, and one
 //    v_dot2_f32_f16 accumulates both tokens' weighted codes in fp32. The constant offset
 //    (the sum of the fp16 weights) is removed once at the end.
 #include "loopkv_internal.h"
@@ -162,28 +162,32 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
   return r;
 }
 struct Masks {
-  uint32_t one, m89, m67;   // fp16 1.0 in both halves; code bits 8..9 / 6..7 of both halves
+  uint32_t one, m89, m67, m45;   // fp16 1.0 in both halves; code bits 8..9 / 6..7 / 4..5 of both
 };
 
+// Offset unit of value channel i (of 16) in dot2_pair: its code sits at mantissa bits 8..9,
+// 6..7 or 4..5, so it enters as 1 + code * kF[i] with kF = 1/4, 1/16 or 1/64.
+__device__ constexpr float kF[8] = {1.f / 64, 1.f / 16, 1.f / 64, 1.f / 16, 1.f / 4, 1.f / 64, 1.f / 16, 1.f / 4};
+
 // acc[c] += w0 * code(t0, c) + w1 * code(t1, c) for the 16 channels of two tokens' 2-bit code
-// words, in offset units: each code enters as the fp16 number 1 + code/4 (even channels) or
-// 1 + code/16 (odd channels).
+// words, in offset units: channel c's code enters as the fp16 number 1 + code * kF[c % 8]. Two
+// shifts of the interleaved word bring all eight codes of a half into mantissa bits 4..9.
 __device__ __forceinline__ void dot2_pair(uint32_t w0, uint32_t w1, half2v wp, const Masks& mk,
                                           float (&acc)[16]) {
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     // channels 8*half .. 8*half+7 of token t0 in bits 0..15, of token t1 in bits 16..31
     const uint32_t s = __builtin_amdgcn_perm(w1, w0, half ? 0x07060302u : 0x05040100u);
-    const uint32_t l4 = s << 4, l8 = s << 8, r4 = s >> 4, r8 = s >> 8;
+    const uint32_t l4 = s << 4, r6 = s >> 6;   // bits 0..3 -> 4..7; bits 10..15 -> 4..9
     float* a = acc + 8 * half;
-    a[0] = dot2(wp, and_or(l8, mk.m89, mk.one), a[0]);
+    a[0] = dot2(wp, and_or(l4, mk.m45, mk.one), a[0]);
     a[1] = dot2(wp, and_or(l4, mk.m67, mk.one), a[1]);
-    a[2] = dot2(wp, and_or(l4, mk.m89, mk.one), a[2]);
+    a[2] = dot2(wp, and_or(s, mk.m45, mk.one), a[2]);
     a[3] = dot2(wp, and_or(s, mk.m67, mk.one), a[3]);
     a[4] = dot2(wp, and_or(s, mk.m89, mk.one), a[4]);
-    a[5] = dot2(wp, and_or(r4, mk.m67, mk.one), a[5]);
-    a[6] = dot2(wp, and_or(r4, mk.m89, mk.one), a[6]);
-    a[7] = dot2(wp, and_or(r8, mk.m67, mk.one), a[7]);
+    a[5] = dot2(wp, and_or(r6, mk.m45, mk.one), a[5]);
+    a[6] = dot2(wp, and_or(r6, mk.m67, mk.one), a[6]);
+    a[7] = dot2(wp, and_or(r6, mk.m89, mk.one), a[7]);
   }
 }
 
@@ -651,6 +655,7 @@ void decode_kernel(DecodeParams prm) {
   k.mk.one = 0x3C003C00u;
   k.mk.m89 = 0x03000300u;
   k.mk.m67 = 0x00C000C0u;
+  k.mk.m45 = 0x00300030u;
 
   WaveState<NVG> st;
   st.M = -INFINITY;
@@ -737,7 +742,7 @@ void decode_kernel(DecodeParams prm) {
         const float p = (ch * kGroup + lane < n_tail) ? fexp2(s2 - st.M) : 0.f;
         st.Lsum += p;
         // odd-channel weight in offset units: (p / VS) * kWScale / 16; even channels 4x that
-        sm.tail_w[w][lane] = p * (kWScale / 16.f / VS);
+        sm.tail_w[w][lane] = p * (kWScale / VS);
       }
       wave_lds_sync();
       for (int j = 0; j < 4; ++j) {
@@ -751,9 +756,9 @@ void decode_kernel(DecodeParams prm) {
         const float wt = sm.tail_w[w][t];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          // exact values, offset-free: even channels weigh 4x the odd ones (f = 1/4 vs 1/16)
-          st.acc[2 * i] = fmaf(4.f * wt, bf16_lo(vv[i]), st.acc[2 * i]);
-          st.acc[2 * i + 1] = fmaf(wt, bf16_hi(vv[i]), st.acc[2 * i + 1]);
+          // exact values, offset-free, in channel c's units (kF[c % 8])
+          st.acc[2 * i] = fmaf(kF[(2 * i) % 8] * wt, bf16_lo(vv[i]), st.acc[2 * i]);
+          st.acc[2 * i + 1] = fmaf(kF[(2 * i + 1) % 8] * wt, bf16_hi(vv[i]), st.acc[2 * i + 1]);
         }
       }
       wave_lds_sync();
@@ -776,8 +781,8 @@ void decode_kernel(DecodeParams prm) {
     v += __shfl_xor(v, 8);
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
-    // offset units: even channels carry code/4, odd code/16, weights x kWScale
-    acc[i] = (v - W) * ((i & 1) ? 16.f : 4.f) * (1.f / kWScale);
+    // offset units: channel i carries code * kF[i % 8], weights x kWScale
+    acc[i] = (v - W) * (1.f / (kF[i % 8] * kWScale));
   }
   if (lane < 8) {
 #pragma unroll
