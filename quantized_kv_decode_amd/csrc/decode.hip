@@ -850,13 +850,13 @@ __global__ __launch_bounds__(kHeadDim) void merge_kernel(Geom g, DecodeCall c) {
 }
 
 // Waves per (request, head) row, which is also the waves per SIMD the register allocation
-// targets: with four rows per workgroup, one workgroup fills a CU. 2-bit cells fit 128 VGPRs
-// (four waves per SIMD); 4-bit cells need more and run three.
+// targets: with four rows per workgroup, one workgroup fills a CU at four waves per SIMD
+// (128 VGPRs).
 #ifndef LOOPKV_NW2
 #define LOOPKV_NW2 4
 #endif
 #ifndef LOOPKV_NW4
-#define LOOPKV_NW4 3
+#define LOOPKV_NW4 4
 #endif
 
 template <int BITS, int P, int RB>

@@ -10,7 +10,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libloopkv.so")
+# The in-tree build; LOOPKV_LIBRARY names another build of the same library (e.g. one compiled
+# with different launch parameters) to load instead.
+LIB_PATH = os.environ.get("LOOPKV_LIBRARY") or os.path.join(HERE, "libloopkv.so")
 
 REUSE, INT2, INT4 = 0, 2, 4
 OK, EINVAL, EPLAN, ENOTSUP, ECAPACITY, EHIP = range(6)
