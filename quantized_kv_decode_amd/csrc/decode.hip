@@ -450,22 +450,27 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   const float rm = row_max16(s2);
   const float gmA = dmax(lane_f(rm, 0), lane_f(rm, 16));
   const float gmB = dmax(lane_f(rm, 32), lane_f(rm, 48));
-  if (lane == 0) {
-    sm.gmax[rd & 1][w][0] = gmA;
-    sm.gmax[rd & 1][w][1] = gmB;
+  // Running maximum before each of the wave's two groups (4-bit history only: 2-bit history
+  // has no low plane to gate, and its waves need not wait for each other).
+  float mpreA = 0.f, mpreB = 0.f;
+  if (BITS == 4) {
+    if (lane == 0) {
+      sm.gmax[rd & 1][w][0] = gmA;
+      sm.gmax[rd & 1][w][1] = gmB;
+    }
+    __syncthreads();
+    // Group maxima of this round in stream order: wave i's groups are 2i and 2i+1.
+    const float* gx = &sm.gmax[rd & 1][0][0];
+    float mall = st.m_run;
+#pragma unroll
+    for (int j = 0; j < 2 * NW; j += 2) mall = dmax3(mall, gx[j], gx[j + 1]);
+    mpreA = dmax(st.m_run, gx[0]);      // everything up to this wave's first group
+#pragma unroll
+    for (int i = 1; i < NW; ++i)
+      if (i <= w) mpreA = dmax3(mpreA, gx[2 * i - 1], gx[2 * i]);
+    mpreB = dmax(mpreA, gmB);
+    st.m_run = mall;
   }
-  __syncthreads();
-  // Group maxima of this round in stream order: wave i's groups are 2i and 2i+1.
-  const float* gx = &sm.gmax[rd & 1][0][0];
-  float mall = st.m_run;
-#pragma unroll
-  for (int j = 0; j < 2 * NW; j += 2) mall = dmax3(mall, gx[j], gx[j + 1]);
-  float mpreA = dmax(st.m_run, gx[0]);      // everything up to this wave's first group
-#pragma unroll
-  for (int i = 1; i < NW; ++i)
-    if (i <= w) mpreA = dmax3(mpreA, gx[2 * i - 1], gx[2 * i]);
-  const float mpreB = dmax(mpreA, gmB);
-  st.m_run = mall;
 
   // ---- last round's low planes, before this round can move the wave's maximum
   if (BITS == 4) add_prev_lo<NVG, NW>(sm, st, (rd + 1) & 1, w, lane, k.mk);
@@ -585,9 +590,10 @@ void decode_kernel(DecodeParams prm) {
   constexpr int NCB = kHeadDim / KCH;
   constexpr float VS = BITS == 4 ? 4.f : 1.f;   // value units of acc: true = VS * code
   static_assert(NW >= 2, "the final merge uses 128 threads");
-  // RB rows (heads of one request) per workgroup, NW waves each. The rows share the round
-  // barrier, which keeps every wave of the CU at the same round: the SIMDs' oldest-first issue
-  // would otherwise run the workgroups one after another and leave the last alone on the CU.
+  // RB rows (heads of one request) per workgroup, NW waves each, one workgroup per CU: with
+  // several workgroups per CU the SIMDs' oldest-first issue runs them one after another and
+  // leaves the last alone on the CU. With 4-bit history the rows also share the round barrier
+  // that the running maximum needs.
   __shared__ Smem<NVG, NW> sm_rows[RB];
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int rsub = wave / NW;
@@ -643,7 +649,7 @@ void decode_kernel(DecodeParams prm) {
   r.err = g.err;
 
   RoundConst k;
-  k.gated = d->gated != 0;
+  k.gated = BITS == 4 && d->gated != 0;
   k.scale2 = c.sm_scale * kLog2e;
   k.log2tau = c.tau > 0.f ? log2f(c.tau) : -INFINITY;
   k.u = u;
