@@ -581,6 +581,8 @@ struct DecodeParams {
 };
 
 
+constexpr int kMaxOrderBatch = 1024;   // larger batches keep the launch order
+
 template <int BITS, int NVG, int P, int NW, int RB>
 __global__ __launch_bounds__(64 * NW * RB) __attribute__((amdgpu_waves_per_eu(NW, NW)))
 void decode_kernel(DecodeParams prm) {
@@ -599,11 +601,35 @@ void decode_kernel(DecodeParams prm) {
   const int rsub = wave / NW;
   Smem<NVG, NW>& sm = sm_rows[rsub];
   const int w = wave - rsub * NW;
-  const int split = blockIdx.x, h = blockIdx.y * RB + rsub, b = blockIdx.z;
+  const int split = blockIdx.x, h = blockIdx.y * RB + rsub;
   const int tid = (int)threadIdx.x - rsub * 64 * NW;   // thread index among the row's waves
   const int lane = tid & 63;
   const LKV_CONST CellDesc* d = as_const(c.desc_dev);
   const int H = g.H;
+  const int64_t cap = min((int64_t)g.max_ctx, (int64_t)c.pt_stride * P);
+
+  // When the launch takes more than one generation of workgroups: longest requests first.
+  // Workgroup z takes the request of rank z by length (descending, ties by index), so the
+  // dispatcher starts the longest rows first and the short ones fill the end of the launch.
+  int b = blockIdx.z;
+  if (c.order_by_len && c.batch > 1 && c.batch <= kMaxOrderBatch) {
+    __shared__ int s_len[kMaxOrderBatch];
+    __shared__ int s_b;
+    for (int i = threadIdx.x; i < c.batch; i += blockDim.x)
+      s_len[i] = (int)min(max((int64_t)as_const(c.seq_lens)[i], (int64_t)0), cap);
+    __syncthreads();
+    for (int i = threadIdx.x; i < c.batch; i += blockDim.x) {
+      const int li = s_len[i];
+      int rank = 0;
+      for (int j = 0; j < c.batch; ++j) {
+        const int lj = s_len[j];
+        rank += (lj > li) | ((lj == li) & (j < i));
+      }
+      if (rank == (int)blockIdx.z) s_b = i;
+    }
+    __syncthreads();
+    b = s_b;
+  }
   const float u = cvt2<false>(1u).x;            // value of fp8 byte 0x01
   const float inv_u = 1.0f / u;
 
@@ -618,7 +644,6 @@ void decode_kernel(DecodeParams prm) {
   if (tid == 0) sm.cnt_hot = 0;
 
   // Row extent.
-  const int64_t cap = min((int64_t)g.max_ctx, (int64_t)c.pt_stride * P);
   int len = as_const(c.seq_lens)[b];
   if (len < 0 || len > cap) {
     if (tid == 0 && split == 0 && h == 0) atomicOr(g.err, (uint32_t)kErrLength);
@@ -869,6 +894,8 @@ template <int BITS, int P, int RB>
 hipError_t launch_bpr(const Geom& g, const DecodeCall& c, hipStream_t stream) {
   DecodeParams prm{g, c};
   const dim3 grid((unsigned)c.n_split, (unsigned)(g.H / RB), (unsigned)c.batch);
+  // one workgroup fills a CU
+  prm.c.order_by_len = (int64_t)grid.x * grid.y * grid.z > (int64_t)g.cus;
   constexpr int kNW = BITS == 2 ? LOOPKV_NW2 : LOOPKV_NW4;
   const unsigned threads = 64 * kNW * RB;
   switch (g.nvg) {

@@ -22,6 +22,7 @@ struct loopkv_plan_s {
   uint32_t* err_dev = nullptr;
   float* partials_dev = nullptr;
   int device = 0;
+  int cus = 0;                    // compute units of that device
 };
 
 namespace {
@@ -152,6 +153,7 @@ Geom make_geom(const loopkv_plan_s* p) {
   g.max_splits = s.max_splits;
   g.num_pages = s.num_pages;
   g.err = p->err_dev;
+  g.cus = p->cus;
   return g;
 }
 
@@ -238,6 +240,7 @@ loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan, v
     }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipGetDevice(&p->device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&p->cus, hipDeviceAttributeMultiprocessorCount, p->device);
   if (e == hipSuccess)
     e = hipMemcpyAsync(p->desc_dev, p->desc.data(), p->desc.size() * sizeof(CellDesc),
                        hipMemcpyHostToDevice, s);
@@ -343,6 +346,7 @@ loopkv_status loopkv_decode_attention(loopkv_plan p, int32_t layer, int32_t loop
   c.stats = o.stats_dev;
   c.out = out;
   c.partials = p->partials_dev;
+  c.order_by_len = 0;   // set by the launcher from the grid size
   hipError_t e = launch_decode(g, p->desc[i], c, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LOOPKV_OK : LOOPKV_EHIP;
 }

@@ -79,6 +79,7 @@ struct Geom {
   int32_t max_splits;
   int64_t num_pages;
   uint32_t* err;         // device error word
+  int32_t cus;           // compute units of the device
 };
 
 // Launchers implemented next to their kernels.
@@ -104,6 +105,7 @@ struct DecodeCall {
   unsigned long long* stats;
   float* out;
   float* partials;        // [batch, H, max_splits, D + 2]
+  int32_t order_by_len;   // launch needs more than one generation: longest requests first
 };
 
 hipError_t launch_decode(const Geom& g, const CellDesc& desc_host, const DecodeCall& c,
