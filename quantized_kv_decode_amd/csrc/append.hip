@@ -64,7 +64,11 @@ __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t flag) { atom
 
 // One workgroup of 128 threads quantizes one completed 32-token key group of one
 // (request, head) into the cell's pool. blockIdx = (group index within this call, head,
-// request).
+// request). With FUSED (calls of at most 32 tokens) the workgroup of group index 0 also copies
+// the call's tokens of its head into the ring and sets the request's quantized-group counter,
+// which saves the separate ring launch on a decode step: the ring slots it writes (positions
+// old .. old+31) never alias the slots the group reads (positions old-31 .. old-1) in a ring of
+// at least 64 tokens.
 // Tokens request b appends in this call: n_new_dev[b] if given (clamped to [0, n_new]).
 __device__ __forceinline__ int appended(const int32_t* n_new_dev, int n_new, int b) {
   if (!n_new_dev) return n_new;
@@ -72,7 +76,7 @@ __device__ __forceinline__ int appended(const int32_t* n_new_dev, int n_new, int
   return m < 0 ? 0 : (m > n_new ? n_new : m);
 }
 
-template <int BITS>
+template <int BITS, bool FUSED>
 __global__ __launch_bounds__(128) void quantize_group_kernel(
     Geom g, const CellDesc* __restrict__ descp, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, int n_new, const int32_t* __restrict__ n_new_dev,
@@ -89,6 +93,16 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
   }
   if (n_new_dev && (n_new_dev[b] < 0 || n_new_dev[b] > n_new) && blockIdx.x == 0 && h == 0 && tid == 0)
     raise_error(g.err, kErrLength);
+  if (FUSED && blockIdx.x == 0) {
+    const int m = (int)(nw - old);
+    for (int i = 0; i < m; ++i) {
+      const size_t src = (((size_t)b * n_new + i) * g.H + h) * g.D + tid;
+      const size_t dst = (((size_t)b * g.tail + (old + i) % g.tail) * g.H + h) * g.D + tid;
+      d.tail_k[dst] = k_new[src];
+      d.tail_v[dst] = v_new[src];
+    }
+    if (h == 0 && tid == 0) d.own_qgroups[b] = (int)(nw / kGroup);
+  }
   const int grp = old / kGroup + (int)blockIdx.x;
   if ((int64_t)(grp + 1) * kGroup > nw) return;
 
@@ -253,15 +267,19 @@ hipError_t launch_append(const Geom& g, const CellDesc* desc_dev, const CellDesc
                          const int32_t* n_new_dev, const int32_t* seq_lens,
                          const int32_t* page_table, int pt_stride, hipStream_t stream) {
   if (dh.own_pool) {
-    const dim3 grid((unsigned)((n_new + kGroup - 1) / kGroup + 1), (unsigned)g.H, (unsigned)batch);
-    if (dh.own_bits == 4)
-      quantize_group_kernel<4><<<grid, 128, 0, stream>>>(g, desc_dev, k_new, v_new, n_new, n_new_dev,
-                                                         seq_lens, page_table, pt_stride);
-    else
-      quantize_group_kernel<2><<<grid, 128, 0, stream>>>(g, desc_dev, k_new, v_new, n_new, n_new_dev,
-                                                         seq_lens, page_table, pt_stride);
+    // A call of n tokens completes at most ceil(n / 32) groups of a request.
+    const dim3 grid((unsigned)((n_new + kGroup - 1) / kGroup), (unsigned)g.H, (unsigned)batch);
+    const bool fused = n_new <= kGroup && g.tail >= 2 * kGroup && g.D == 128;
+    if (dh.own_bits == 4) {
+      if (fused) quantize_group_kernel<4, true><<<grid, 128, 0, stream>>>(g, desc_dev, k_new, v_new, n_new, n_new_dev, seq_lens, page_table, pt_stride);
+      else quantize_group_kernel<4, false><<<grid, 128, 0, stream>>>(g, desc_dev, k_new, v_new, n_new, n_new_dev, seq_lens, page_table, pt_stride);
+    } else {
+      if (fused) quantize_group_kernel<2, true><<<grid, 128, 0, stream>>>(g, desc_dev, k_new, v_new, n_new, n_new_dev, seq_lens, page_table, pt_stride);
+      else quantize_group_kernel<2, false><<<grid, 128, 0, stream>>>(g, desc_dev, k_new, v_new, n_new, n_new_dev, seq_lens, page_table, pt_stride);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (fused) return hipSuccess;
   }
   // The ring kernel must follow the quantize kernel: that one reads ring slots this one
   // may overwrite. Both are on `stream`, so they run in order.
