@@ -83,7 +83,7 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table, int pt_stride) {
   constexpr int L = (1 << BITS) - 1;
   const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const CellDesc& d = *descp;
+  const CellDesc d = *descp;   // a copy: the stores below cannot alias it
   const int old = seq_lens[b];
   const int64_t nw = (int64_t)old + appended(n_new_dev, n_new, b);
   const int64_t cap = min((int64_t)g.max_ctx, (int64_t)pt_stride * g.P);
@@ -115,21 +115,28 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
 
   const int H = g.H, D = g.D;
   // Stage the group's 32 tokens: positions before `old` come from the ring, later ones
-  // from this call's input. Each wave reads whole 256-byte rows.
-  for (int t = 0; t < kGroup; ++t) {
-    const int pos = grp * kGroup + t;
-    const uint16_t *kp, *vp;
-    if (pos >= old) {
-      const size_t row = ((size_t)b * n_new + (pos - old)) * H + h;
-      kp = k_new + row * D;
-      vp = v_new + row * D;
-    } else {
-      const size_t row = ((size_t)b * g.tail + (pos % g.tail)) * H + h;
-      kp = d.tail_k + row * D;
-      vp = d.tail_v + row * D;
+  // from this call's input. Each wave reads whole 256-byte rows; all 64 loads are issued
+  // before the first LDS store, so the staging costs one memory latency, not 32.
+  {
+    typedef const __attribute__((address_space(1))) uint16_t* gu16;
+    uint16_t kr[kGroup], vr[kGroup];
+    const int slot0 = (grp * kGroup) % g.tail;   // ring slot of the group's first token
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+      const int pos = grp * kGroup + t;
+      const bool fresh = pos >= old;
+      int slot = slot0 + t;
+      if (slot >= g.tail) slot -= g.tail;
+      const size_t row = fresh ? ((size_t)b * n_new + (pos - old)) * H + h
+                               : ((size_t)b * g.tail + slot) * H + h;
+      kr[t] = ((gu16)(fresh ? k_new : d.tail_k))[row * D + tid];
+      vr[t] = ((gu16)(fresh ? v_new : d.tail_v))[row * D + tid];
     }
-    ks[t][tid] = bf16_to_f32(kp[tid]);
-    vs[t][tid] = bf16_to_f32(vp[tid]);
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+      ks[t][tid] = bf16_to_f32(kr[t]);
+      vs[t][tid] = bf16_to_f32(vr[t]);
+    }
   }
   // Physical pages holding the group (one for 32-token pages, two for 16-token pages).
   if (tid < kGroup / g.P) {
