@@ -50,20 +50,22 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def build_cache(name, seed, tau):
+def build_cache(name, seed, tau, plan_name="seeded", v_group=128):
     import torch
     from quantized_kv_decode_amd import loopkv as L
     from quantized_kv_decode_amd import synth
     from quantized_kv_decode_amd.cache import LoopKVCache
 
     layers, loops, B, N, p4, pr, split, heavy = WORKLOADS[name]
-    if p4 is None:
+    if plan_name != "seeded":
+        plan = synth.named_plan(plan_name, layers, loops)
+    elif p4 is None:
         plan = np.array([[4], [4], [2], [4]], np.uint8)
     else:
         plan = synth.plan(layers, loops, seed, p4, pr)
     P = 32
     pages_per_seq = N // P
-    shape = L.make_shape(num_layers=layers, num_loops=loops, page_tokens=P, v_group=128, max_batch=B,
+    shape = L.make_shape(num_layers=layers, num_loops=loops, page_tokens=P, v_group=v_group, max_batch=B,
                          max_pages_per_seq=pages_per_seq, tail_tokens=64,
                          max_splits=max(1, N // split) if split else 1, num_pages=B * pages_per_seq)
     cache = LoopKVCache(shape, plan)
@@ -102,7 +104,7 @@ def run_step(cache, plan, qs, outs, seq, pt, tau, split, stats=None, events=None
             i += 1
 
 
-def algorithmic_bytes(plan, hot_frac, B, N, H=16, n_split=1):
+def algorithmic_bytes(plan, hot_frac, B, N, H=16, n_split=1, v_group=128):
     """Bytes one decode step reads/writes by the path's definition: per history (token, head)
     116 + 32*h bytes for an INT4-read cell and 84 for an INT2-read cell, plus q, out, the
     page table, and split partials."""
@@ -113,7 +115,8 @@ def algorithmic_bytes(plan, hot_frac, B, N, H=16, n_split=1):
     for t in range(loops):
         for l in range(layers):
             src = plan[loops - 1, l] if plan[t, l] == 0 else plan[t, l]
-            per_tok = INT4_BASE + INT4_LO * hot_frac[i] if src == 4 else INT2_BYTES
+            vsz = 4 * 128 / v_group - 4          # value scale/zero beyond the 128-channel case
+            per_tok = INT4_BASE + vsz + INT4_LO * hot_frac[i] if src == 4 else INT2_BYTES + vsz
             b = B * N * H * per_tok + B * H * 128 * (2 + 4) + B * (N // 32) * 4
             if n_split > 1:
                 b += 2 * B * H * n_split * 130 * 4
@@ -403,6 +406,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--plan", default="seeded",
+                    choices=["seeded", "kivi4", "kivi4_loop3_share", "int2_loops123", "loopkv_r", "loopkv_m"],
+                    help="the workload's seeded plan, or one of the paper's fixed plans")
+    ap.add_argument("--v-group", type=int, default=128, choices=[128, 64, 32])
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -417,7 +424,7 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == PAGED:
         return run_paged(args)
-    cache, plan, pt, pt_np, cfg = build_cache(args.workload, args.seed, args.tau)
+    cache, plan, pt, pt_np, cfg = build_cache(args.workload, args.seed, args.tau, args.plan, args.v_group)
     loops, layers = plan.shape
     B, N, split = cfg["B"], cfg["N"], cfg["split"]
     ncell = loops * layers
@@ -479,7 +486,7 @@ def main():
         med_ms = graph_ms
 
     n_split = (N + split - 1) // split if split else 1
-    alg_bytes, per_cell_bytes = algorithmic_bytes(plan, hot_frac, B, N, n_split=n_split)
+    alg_bytes, per_cell_bytes = algorithmic_bytes(plan, hot_frac, B, N, n_split=n_split, v_group=args.v_group)
     # Dominant kernel: the INT4-read decode (own INT4 cells and cells reusing an INT4 source).
     src_bits = np.array([plan[loops - 1, l] if plan[t, l] == 0 else plan[t, l]
                          for t in range(loops) for l in range(layers)])
@@ -498,7 +505,8 @@ def main():
     tfile = os.path.join(ROOT, "profiles", "decode_traffic.json")
     if os.path.exists(tfile):
         tj = json.load(open(tfile))
-        if tj.get("kernel_hash") == kernel_hash() and tj.get("workload") == args.workload:
+        if (tj.get("kernel_hash") == kernel_hash() and tj.get("workload") == args.workload
+                and args.plan == "seeded" and args.v_group == 128):
             traffic = tj.get("hbm_bytes_per_launch")
 
     cpu = None
@@ -523,7 +531,7 @@ def main():
                    "split_tokens": split, "plan_counts": {"int4": int((plan == 4).sum()),
                                                           "int2": int((plan == 2).sum()),
                                                           "reuse": int((plan == 0).sum())},
-                   "page_tokens": 32, "v_group": 128, "plan_seed": args.seed},
+                   "page_tokens": 32, "v_group": args.v_group, "plan": args.plan, "plan_seed": args.seed},
         "achieved_TBps": round(alg_bytes / (med_ms / 1e3) / 1e12, 3),
         "hot_fraction": round(overall_hot, 4),
         "alg_bytes_per_step": int(alg_bytes),

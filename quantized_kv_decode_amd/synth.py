@@ -94,6 +94,35 @@ def plan(num_layers: int, num_loops: int, seed: int, p_int4: float, p_reuse: flo
     return p
 
 
+def named_plan(name: str, num_layers: int, num_loops: int) -> np.ndarray:
+    """The paper's fixed plans by name (uint8 [num_loops, num_layers], final loop never REUSE):
+    "kivi4" every cell INT4; "kivi4_loop3_share" loop 3 reuses the final loop's KV;
+    "int2_loops123" INT2 before the final loop; "loopkv_r" 25 of the 72 cells before the final
+    loop INT2, taken in loop-major order from the first and last 6 layers; "loopkv_m" the first
+    26 of those 72 cells (loop-major) reuse the final loop, the next 20 are INT2."""
+    p = np.full((num_loops, num_layers), INT4, dtype=np.uint8)
+    early = [(t, l) for t in range(num_loops - 1) for l in range(num_layers)]
+    if name == "kivi4":
+        pass
+    elif name == "kivi4_loop3_share":
+        p[num_loops - 2, :] = REUSE
+    elif name == "int2_loops123":
+        p[:num_loops - 1, :] = INT2
+    elif name == "loopkv_r":
+        edge = list(range(6)) + list(range(num_layers - 6, num_layers))
+        cells = [(t, l) for t in range(num_loops - 1) for l in edge]
+        for t, l in cells[:25]:
+            p[t, l] = INT2
+    elif name == "loopkv_m":
+        for t, l in early[:26]:
+            p[t, l] = REUSE
+        for t, l in early[26:46]:
+            p[t, l] = INT2
+    else:
+        raise ValueError(f"unknown plan {name!r}")
+    return p
+
+
 def lengths(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
     """int32 per-request context lengths, uniform on [lo, hi]."""
     rng = np.random.default_rng(seed)

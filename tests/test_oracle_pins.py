@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import oracle as O
+from quantized_kv_decode_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -327,22 +328,9 @@ def test_page_table_invariance(P):
 
 # ------------------------------------------------------------------ byte model
 def _plan(name, layers, loops):
-    p = np.full((loops, layers), 4, dtype=np.uint8)
-    if name == "int4_loop3_reuse":
-        p[2, :] = 0
-    elif name == "int2_loops123":
-        p[:3, :] = 2
-    elif name == "loopkv_r":          # 25 of the 72 history cells INT2, in the first/last 6 layers
-        cells = [(t, l) for t in range(3) for l in list(range(6)) + list(range(18, 24))]
-        for t, l in cells[:25]:
-            p[t, l] = 2
-    elif name == "loopkv_m":          # 26 shared, 20 own INT2, 50 INT4 (loop 4 all INT4)
-        flat = [(t, l) for t in range(3) for l in range(layers)]
-        for t, l in flat[:26]:
-            p[t, l] = 0
-        for t, l in flat[26:46]:
-            p[t, l] = 2
-    return p
+    names = {"all_int4": "kivi4", "int4_loop3_reuse": "kivi4_loop3_share", "int2_loops123": "int2_loops123",
+             "loopkv_r": "loopkv_r", "loopkv_m": "loopkv_m"}
+    return synth.named_plan(names[name], layers, loops)
 
 
 def test_cache_bytes_match_paper_figures():
