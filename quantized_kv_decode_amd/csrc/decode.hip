@@ -907,11 +907,14 @@ hipError_t launch_bpr(const Geom& g, const DecodeCall& c, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Four heads per workgroup when the head count allows (one workgroup per CU at 3 waves per
-// SIMD), else one.
+// Four heads per workgroup (one workgroup per CU) when the head count allows and that still
+// gives every CU a workgroup; otherwise one head per workgroup, so a small launch (few requests,
+// short rows) spreads over four times as many CUs.
 template <int BITS, int P>
 hipError_t launch_bp(const Geom& g, const DecodeCall& c, hipStream_t stream) {
-  return g.H % 4 == 0 ? launch_bpr<BITS, P, 4>(g, c, stream) : launch_bpr<BITS, P, 1>(g, c, stream);
+  const int64_t wg4 = (int64_t)c.n_split * (g.H / 4) * c.batch;
+  return g.H % 4 == 0 && wg4 >= g.cus ? launch_bpr<BITS, P, 4>(g, c, stream)
+                                       : launch_bpr<BITS, P, 1>(g, c, stream);
 }
 
 }  // namespace
