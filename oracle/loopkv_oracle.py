@@ -19,7 +19,12 @@ Functions and what pins them (tests/test_oracle_pins.py):
   split_planes / dequant_*          -- bijection c = 4*hi + lo, cold error (1.5 - lo)*s
   fetch_mask                        -- tau=0 all hot, tau>1 all cold, conservativeness
                                       against the global row max (Proposition 1's proof),
-                                      a non-streaming brute force on tiny rows
+                                      a non-streaming brute force on tiny rows (also with
+                                      the history starting after a sink)
+  near_far_split                    -- token-by-token enumeration of the window rule
+  decode_head with a sink           -- library attention over sink + history + window,
+                                      closed-form all-cold row under a dominant sink,
+                                      seed monotonicity
   attention_row / decode_cell       -- library softmax attention (torch SDPA in fp64) at
                                       tau=0 and tau>1, one token, zero query, the
                                       Proposition-1 error bound, split and page invariance
@@ -149,14 +154,27 @@ def dequant_values_cold(codes4, s, z):
 # Read-time V precision mask (§3.3; §3.4 "One launch per cell"; Appendix "Proof of
 # Proposition 1")
 # --------------------------------------------------------------------------------------
-def fetch_mask(scores, m0, tau, split_tokens=0, group=K_GROUP):
+def _split_groups(n, start, split_tokens, group):
+    """Yields (g0, g1, new_split) for the 32-token groups of a history slice of n scores whose
+    first score is absolute token `start`; new_split marks the first group of each split.
+    Splits are runs of split_tokens tokens counted from token 0 of the request (0: one split)."""
+    prev = None
+    for g0 in range(0, n, group):
+        sp = (start + g0) // split_tokens if split_tokens else 0
+        yield g0, min(g0 + group, n), sp != prev
+        prev = sp
+
+
+def fetch_mask(scores, m0, tau, split_tokens=0, group=K_GROUP, start=0):
     """Which history tokens read the low plane (True = hot).
 
-    scores: float64 [n] (n a multiple of `group`), the attention logits of one row.
-    The row is cut into splits of `split_tokens` tokens from token 0 (0 means one split).
-    Within a split, a running maximum starts at the seed m0 (-inf when there is none) and,
-    group by group in order, first absorbs the group's largest score, then tests the
-    group's tokens: a token is cold iff exp(s_j - m) < tau.
+    scores: float64 [n] (n a multiple of `group`), the attention logits of the history
+    tokens start, start + 1, ... of one row (start a multiple of `group`: 0, or the sink
+    length when a sink precedes the history). The request is cut into splits of
+    `split_tokens` tokens from token 0 (0 means one split). Within a split, a running
+    maximum starts at the seed m0 (-inf when there is none) and, group by group in order,
+    first absorbs the group's largest score, then tests the group's tokens: a token is cold
+    iff exp(s_j - m) < tau.
 
     Reading: the paper ties the running maximum to the kernel's stream order, and the kernel
     has every key code of a page (hence every score of the page) before it touches the
@@ -164,32 +182,50 @@ def fetch_mask(scores, m0, tau, split_tokens=0, group=K_GROUP):
     any tau > 1 read none.
     """
     scores = np.asarray(scores, dtype=np.float64)
-    n = scores.shape[0]
-    hot = np.ones(n, dtype=bool)
-    step = split_tokens if split_tokens else max(n, 1)
-    for s0 in range(0, n, step):
-        m = m0
-        for g0 in range(s0, min(s0 + step, n), group):
-            g1 = min(g0 + group, s0 + step, n)
-            m = max(m, float(scores[g0:g1].max()))
-            hot[g0:g1] = ~(np.exp(scores[g0:g1] - m) < tau)
+    hot = np.ones(scores.shape[0], dtype=bool)
+    m = m0
+    for g0, g1, new_split in _split_groups(scores.shape[0], start, split_tokens, group):
+        if new_split:
+            m = m0
+        m = max(m, float(scores[g0:g1].max()))
+        hot[g0:g1] = ~(np.exp(scores[g0:g1] - m) < tau)
     return hot
 
 
-def tie_mask(scores, m0, tau, split_tokens=0, group=K_GROUP, band=1e-6):
+def tie_mask(scores, m0, tau, split_tokens=0, group=K_GROUP, band=1e-6, start=0):
     """Tokens whose test value exp(s_j - m) lies within `band` of tau: their hot/cold
     decision may differ between fp64 and a kernel's fp32 arithmetic."""
     scores = np.asarray(scores, dtype=np.float64)
-    n = scores.shape[0]
-    tie = np.zeros(n, dtype=bool)
-    step = split_tokens if split_tokens else max(n, 1)
-    for s0 in range(0, n, step):
-        m = m0
-        for g0 in range(s0, min(s0 + step, n), group):
-            g1 = min(g0 + group, s0 + step, n)
-            m = max(m, float(scores[g0:g1].max()))
-            tie[g0:g1] = np.abs(np.exp(scores[g0:g1] - m) - tau) <= band
+    tie = np.zeros(scores.shape[0], dtype=bool)
+    m = m0
+    for g0, g1, new_split in _split_groups(scores.shape[0], start, split_tokens, group):
+        if new_split:
+            m = m0
+        m = max(m, float(scores[g0:g1].max()))
+        tie[g0:g1] = np.abs(np.exp(scores[g0:g1] - m) - tau) <= band
     return tie
+
+
+# --------------------------------------------------------------------------------------
+# Sink and window (§2.3 "Measuring KV damage"; §3.2 "Cross-loop KV sharing"; §3.4 "The
+# unified kernel", "Layout")
+# --------------------------------------------------------------------------------------
+def near_far_split(n, sink_tokens=0, window_tokens=0, group=K_GROUP):
+    """Which positions of a request holding n tokens are quantized history and which stay
+    exact (bf16).
+
+    The first `sink_tokens` positions are the sink and stay exact. A `group`-token page past
+    the sink is quantized once it has left the window, i.e. once none of its tokens is among
+    the last `window_tokens` positions; until then it is exact. With no sink and no window
+    this is "quantize a group as soon as it is complete".
+    Returns (sink_end, hist_begin, hist_end): the sink is [0, sink_end), the quantized history
+    [hist_begin, hist_end) (whole groups, possibly empty), the exact rest [hist_end, n) when
+    n > hist_end.
+    """
+    assert sink_tokens % group == 0 and window_tokens % group == 0
+    hs = sink_tokens // group
+    he = max(hs, (n - window_tokens) // group)
+    return min(n, sink_tokens), hs * group, he * group
 
 
 # --------------------------------------------------------------------------------------
@@ -225,25 +261,37 @@ def quantize_head(k, v, bits, v_group):
 
 
 def decode_head(q, qh: QuantHead | None, tail_k, tail_v, *, sm_scale, tau, m0=-math.inf,
-                split_tokens=0):
+                split_tokens=0, sink_k=None, sink_v=None, hist_start=0, sink_seed=True):
     """One (request, head) of one decode call.
 
     q: float64 [D] (exact bf16 query values). qh: the quantized history the cell reads
     (its own, or for a cell that reuses the final loop's KV, the final loop's at the same
-    layer -- §3.2: it attends with its own query over that history). tail_k/tail_v:
-    float64 [t, D], exact bf16 tokens that are not quantized yet.
+    layer -- §3.2: it attends with its own query over that history), covering the tokens
+    hist_start, hist_start + 1, ... tail_k/tail_v: float64 [t, D], exact bf16 tokens after
+    the history (the window, or the tokens not quantized yet). sink_k/sink_v: float64
+    [s, D], the exact sink tokens before the history, or None.
 
     Scores s_j = sm_scale * q . K^_j. INT4 history reads values at full precision for hot
     tokens and at the bucket midpoint for cold ones (fetch_mask); INT2 history has no mask.
+    The running maximum of the mask starts at m0 joined with the largest sink score (§3.4:
+    the near part publishes the sink maximum as the far part's seed; sink_seed=False keeps
+    m0 alone). Reading: the pages fall back to -inf when the published maximum is late; here
+    it is always used, so the mask is deterministic.
     Returns (out [D], hot [n_hist] bool, scores [n_hist]).
     """
     q = np.asarray(q, dtype=np.float64)
     d = q.shape[0]
+    sink_k = np.zeros((0, d)) if sink_k is None else np.asarray(sink_k, dtype=np.float64).reshape(-1, d)
+    sink_v = np.zeros((0, d)) if sink_v is None else np.asarray(sink_v, dtype=np.float64).reshape(-1, d)
+    s_sink = sm_scale * (sink_k @ q)
+    seed = m0
+    if sink_seed and s_sink.size:
+        seed = max(seed, float(s_sink.max()))
     if qh is not None and qh.k_codes.shape[0] > 0:
         khat = dequant_keys(qh.k_codes, qh.k_s, qh.k_z)
         s_hist = sm_scale * (khat @ q)
         if qh.bits == INT4:
-            hot = fetch_mask(s_hist, m0, tau, split_tokens)
+            hot = fetch_mask(s_hist, seed, tau, split_tokens, start=hist_start)
             vfull = dequant_values_full(qh.v_codes, qh.v_s, qh.v_z)
             vcold = dequant_values_cold(qh.v_codes, qh.v_s, qh.v_z)
             vhat = np.where(hot[:, None], vfull, vcold)
@@ -257,7 +305,8 @@ def decode_head(q, qh: QuantHead | None, tail_k, tail_v, *, sm_scale, tau, m0=-m
     tail_k = np.asarray(tail_k, dtype=np.float64).reshape(-1, d)
     tail_v = np.asarray(tail_v, dtype=np.float64).reshape(-1, d)
     s_tail = sm_scale * (tail_k @ q)
-    out = attention_row(np.concatenate([s_hist, s_tail]), np.concatenate([vhat, tail_v]))
+    out = attention_row(np.concatenate([s_sink, s_hist, s_tail]),
+                        np.concatenate([sink_v, vhat, tail_v]))
     return out, hot, s_hist
 
 
@@ -384,12 +433,13 @@ def unpack_head_block(bits, page_tokens, buf, d=128, v_group=128):
 
 
 def pack_pool(bits, page_tokens, heads_q: list[list[QuantHead]], page_table, num_pages,
-              v_group=128):
+              v_group=128, hist_start=0):
     """The expected bytes of one cell's pool.
 
-    heads_q[b][h]: the quantized history of request b, head h (whole groups). page_table:
-    int [B, stride], logical page -> physical page id. Pages never written stay zero.
-    Returns uint8 [num_pages, page_bytes].
+    heads_q[b][h]: the quantized history of request b, head h (whole groups) covering the
+    tokens hist_start, hist_start + 1, ... (hist_start a multiple of 32: the sink length).
+    page_table: int [B, stride], logical page -> physical page id. Pages never written stay
+    zero. Returns uint8 [num_pages, page_bytes].
     """
     nb = len(heads_q)
     nh = len(heads_q[0]) if nb else 0
@@ -409,19 +459,19 @@ def pack_pool(bits, page_tokens, heads_q: list[list[QuantHead]], page_table, num
                                       qh.v_s[rows], qh.v_z[rows],
                                       qh.k_s[g] if starts else None,
                                       qh.k_z[g] if starts else None, v_group)
-                pid = int(page_table[b][lp])
+                pid = int(page_table[b][(hist_start + t0) // page_tokens])
                 pool[pid, h * hb:(h + 1) * hb] = blk
     return pool
 
 
 def unpack_pool_head(bits, page_tokens, pool, page_table_row, n_tokens, h, num_heads,
-                     d=128, v_group=128) -> QuantHead:
-    """Read one (request, head)'s quantized history (n_tokens, whole groups) back out of a
-    pool's bytes through its page-table row."""
+                     d=128, v_group=128, hist_start=0) -> QuantHead:
+    """Read one (request, head)'s quantized history (n_tokens, whole groups, starting at token
+    hist_start) back out of a pool's bytes through its page-table row."""
     hb = head_block_layout(bits, page_tokens, d, v_group)["total"][1]
     kc, vc, vs, vz, ks, kz = [], [], [], [], [], []
     for lp in range(n_tokens // page_tokens):
-        pid = int(page_table_row[lp])
+        pid = int(page_table_row[(hist_start + lp * page_tokens) // page_tokens])
         blk = pool[pid, h * hb:(h + 1) * hb]
         u = unpack_head_block(bits, page_tokens, blk, d, v_group)
         kc.append(u["k_codes"]); vc.append(u["v_codes"]); vs.append(u["v_s"]); vz.append(u["v_z"])

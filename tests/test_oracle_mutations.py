@@ -47,7 +47,7 @@ def _cold_midpoint_2(codes4, s, z):
     return M._rep_v(s, codes4.shape[1]) * (4.0 * hi + 2.0) + M._rep_v(z, codes4.shape[1])
 
 
-def _mask_le(scores, m0, tau, split_tokens=0, group=32):
+def _mask_le(scores, m0, tau, split_tokens=0, group=32, start=0):
     scores = np.asarray(scores, dtype=np.float64)
     n = len(scores); hot = np.ones(n, dtype=bool); step = split_tokens or max(n, 1)
     for s0 in range(0, n, step):
@@ -59,7 +59,7 @@ def _mask_le(scores, m0, tau, split_tokens=0, group=32):
     return hot
 
 
-def _mask_max_after_test(scores, m0, tau, split_tokens=0, group=32):
+def _mask_max_after_test(scores, m0, tau, split_tokens=0, group=32, start=0):
     scores = np.asarray(scores, dtype=np.float64)
     n = len(scores); hot = np.ones(n, dtype=bool); step = split_tokens or max(n, 1)
     for s0 in range(0, n, step):
@@ -72,8 +72,28 @@ def _mask_max_after_test(scores, m0, tau, split_tokens=0, group=32):
     return hot
 
 
-def _mask_no_split_reset(scores, m0, tau, split_tokens=0, group=32):
+def _mask_no_split_reset(scores, m0, tau, split_tokens=0, group=32, start=0):
     return M.__dict__["_orig_fetch_mask"](scores, m0, tau, 0, group)
+
+
+def _mask_splits_from_history_start(scores, m0, tau, split_tokens=0, group=32, start=0):
+    return M.__dict__["_orig_fetch_mask"](scores, m0, tau, split_tokens, group, start=0)
+
+
+def _window_exit_when_page_starts_leaving(n, sink_tokens=0, window_tokens=0, group=32):
+    hs = sink_tokens // group
+    he = max(hs, (n - window_tokens + group - 1) // group)
+    return min(n, sink_tokens), hs * group, he * group
+
+
+def _decode_head_sink_not_seeding(*a, **kw):
+    kw["sink_seed"] = False
+    return M.__dict__["_orig_decode_head"](*a, **kw)
+
+
+def _decode_head_sink_dropped(*a, **kw):
+    kw["sink_k"] = kw["sink_v"] = None
+    return M.__dict__["_orig_decode_head"](*a, **kw)
 
 
 def _pack_rowmajor(codes, per_word, width):
@@ -121,6 +141,15 @@ MUTANTS = {
                              [P.test_attention_special_cases], []),
     "key scale bytes dropped": ("token_head_bytes", _token_bytes_no_ksz,
                                 [P.test_cache_bytes_match_paper_figures], []),
+    "splits counted from the history start": ("fetch_mask", _mask_splits_from_history_start,
+                                              [P.test_mask_after_sink_matches_brute_force], [32, 64]),
+    "page quantized when it starts leaving the window": (
+        "near_far_split", _window_exit_when_page_starts_leaving,
+        [P.test_near_far_split_enumeration], [32, 256]),
+    "sink maximum not used as the seed": ("decode_head", _decode_head_sink_not_seeding,
+                                          [P.test_dominant_sink_seed_makes_history_cold], []),
+    "sink left out of the softmax": ("decode_head", _decode_head_sink_dropped,
+                                     [P.test_sink_window_attention_reduces_to_library_sdpa], [4, 0.0]),
 }
 
 
@@ -129,6 +158,7 @@ def test_pins_catch_mutant(name, monkeypatch):
     attr, mutant, pins, args = MUTANTS[name]
     monkeypatch.setitem(M.__dict__, "_orig_fetch_mask", M.fetch_mask)
     monkeypatch.setitem(M.__dict__, "_orig_token_head_bytes", M.token_head_bytes)
+    monkeypatch.setitem(M.__dict__, "_orig_decode_head", M.decode_head)
     monkeypatch.setattr(M, attr, mutant)
     monkeypatch.setattr(O, attr, mutant, raising=False)
     caught = []

@@ -133,16 +133,19 @@ def test_planes_bijection_and_cold_error():
 
 
 # ------------------------------------------------------------------ mask
-def _brute_mask(scores, m0, tau, split, group=32):
-    """Non-streaming: token j's reference maximum is the seed joined with every score of its
-    split up to the end of its own group."""
+def _brute_mask(scores, m0, tau, split, group=32, start=0):
+    """Non-streaming: history token j sits at absolute position start + j; its reference
+    maximum is the seed joined with every history score of its split (runs of `split` tokens
+    from position 0) up to the end of its own group."""
     n = len(scores)
-    step = split or n
     hot = np.zeros(n, dtype=bool)
     for j in range(n):
-        s0 = (j // step) * step
-        gend = min(((j - s0) // group + 1) * group + s0, s0 + step, n)
-        m = max([m0] + list(scores[s0:gend]))
+        a = start + j
+        s_lo, s_hi = ((a // split) * split, (a // split + 1) * split) if split else (0, start + n)
+        g_hi = (a // group + 1) * group
+        lo = max(s_lo, start) - start
+        hi = min(g_hi, s_hi, start + n) - start
+        m = max([m0] + list(scores[lo:hi]))
         hot[j] = math.exp(scores[j] - m) >= tau
     return hot
 
@@ -154,6 +157,18 @@ def test_mask_matches_non_streaming_brute_force(split, tau, m0):
     rng = np.random.default_rng(4)
     scores = rng.standard_normal(192) * 3
     assert np.array_equal(O.fetch_mask(scores, m0, tau, split), _brute_mask(scores, m0, tau, split))
+
+
+@pytest.mark.parametrize("start", [32, 96])
+@pytest.mark.parametrize("split", [0, 64, 128])
+def test_mask_after_sink_matches_brute_force(start, split):
+    """History that starts after a sink: splits still count from token 0, so the first split
+    holds fewer history groups."""
+    rng = np.random.default_rng(41)
+    scores = rng.standard_normal(256) * 3
+    for tau in [0.01, 0.1]:
+        got = O.fetch_mask(scores, -math.inf, tau, split, start=start)
+        assert np.array_equal(got, _brute_mask(scores, -math.inf, tau, split, start=start))
 
 
 def test_mask_identities_and_conservativeness():
@@ -362,3 +377,98 @@ def test_cache_bytes_baseline_shapes():
     assert r["stored"] == 16 * (148 + 84 + 148)
     assert r["read_all_hot"] == 16 * (148 + 84 + 148 + 148)
     assert r["read_all_hot"] - r["read_hi_only"] == 16 * 32 * 3
+
+
+# ------------------------------------------------------------------ sink and window
+def _brute_quantized_groups(n, S, W):
+    """Token by token: a 32-token group past the sink is quantized iff it is complete and none
+    of its tokens is among the last W positions."""
+    return {g for g in range(S // 32, n // 32)
+            if all(p < n and p < n - W for p in range(32 * g, 32 * g + 32))}
+
+
+@pytest.mark.parametrize("S", [0, 32])
+@pytest.mark.parametrize("W", [0, 32, 64, 256])
+def test_near_far_split_enumeration(S, W):
+    for n in range(0, 640):
+        sink_end, hb, he = O.near_far_split(n, S, W)
+        assert sink_end == min(n, S)
+        groups = _brute_quantized_groups(n, S, W)
+        assert set(range(hb // 32, he // 32)) == groups
+        if groups:
+            assert hb == S and W <= n - he <= W + 31
+        else:
+            assert he == hb == S
+
+
+def _sink_row(rng, n_sink, n_hist, n_win, bits, outliers=True):
+    ks, vs = rand_bf16(rng, n_sink, 128), rand_bf16(rng, n_sink, 128)
+    _, _, qh = _head(rng, n_hist, bits, outliers=outliers)
+    kw, vw = rand_bf16(rng, n_win, 128), rand_bf16(rng, n_win, 128)
+    return ks, vs, qh, kw, vw
+
+
+@pytest.mark.parametrize("bits,tau", [(4, 0.0), (4, 2.0), (2, 0.05)])
+def test_sink_window_attention_reduces_to_library_sdpa(bits, tau):
+    """Sink, history and window together: at the identity taus (and on INT2) the output is a
+    library softmax attention over [sink exact; history dequantized; window exact]."""
+    rng = np.random.default_rng(42)
+    ks, vs, qh, kw, vw = _sink_row(rng, 32, 128, 37, bits)
+    q = rand_bf16(rng, 128)
+    out, hot, _ = O.decode_head(q, qh, kw, vw, sm_scale=1 / math.sqrt(128), tau=tau,
+                                sink_k=ks, sink_v=vs, hist_start=32)
+    khat = O.dequant_keys(qh.k_codes, qh.k_s, qh.k_z)
+    if bits == 4 and tau > 1:
+        vhat = O.dequant_values_cold(qh.v_codes, qh.v_s, qh.v_z)
+        assert not hot.any()
+    else:
+        vhat = O.dequant_values_full(qh.v_codes, qh.v_s, qh.v_z)
+        assert hot.all()
+    ref = _sdpa(q, np.concatenate([ks, khat, kw]), np.concatenate([vs, vhat, vw]))
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+    # a window that covers the whole request: exact attention over every token
+    out2, hot2, _ = O.decode_head(q, None, kw, vw, sm_scale=1 / math.sqrt(128), tau=tau,
+                                  sink_k=ks, sink_v=vs, hist_start=32)
+    assert hot2.size == 0
+    assert np.allclose(out2, _sdpa(q, np.concatenate([ks, kw]), np.concatenate([vs, vw])),
+                       rtol=1e-12, atol=1e-12)
+
+
+def test_dominant_sink_seed_makes_history_cold():
+    """A sink key aligned with the query scores far above every history token, so with the
+    sink maximum as the seed every history token is cold (exp(s_j - m) < tau from the first
+    group on); without it each split's largest score is hot."""
+    rng = np.random.default_rng(43)
+    ks, vs, qh, kw, vw = _sink_row(rng, 32, 192, 5, 4, outliers=False)
+    q = np.zeros(128)
+    q[:8] = 1.0
+    ks[3] = 0.0
+    ks[3, :8] = 64.0                      # score 512 / sqrt(128) = 45.25 vs |history| < 10
+    sm = 1 / math.sqrt(128)
+    _, hot, s_hist = O.decode_head(q, qh, kw, vw, sm_scale=sm, tau=0.01, sink_k=ks, sink_v=vs,
+                                   hist_start=32, split_tokens=64)
+    assert s_hist.max() < 45.25 + math.log(0.01)
+    assert not hot.any()
+    _, hot0, _ = O.decode_head(q, qh, kw, vw, sm_scale=sm, tau=0.01, sink_k=ks, sink_v=vs,
+                               hist_start=32, split_tokens=64, sink_seed=False)
+    # splits of 64 from token 0 with the history at 32..223: splits [32,64), [64,128),
+    # [128,192), [192,224); each has its largest score hot
+    for lo, hi in [(0, 32), (32, 96), (96, 160), (160, 192)]:
+        assert hot0[lo + int(np.argmax(s_hist[lo:hi]))]
+
+
+def test_sink_seed_monotone_and_proposition1():
+    """A larger seed only turns hot tokens cold; with the sink maximum as the seed every cold
+    token still weighs less than tau times the largest weight of the whole row."""
+    rng = np.random.default_rng(44)
+    for trial in range(12):
+        ks, vs, qh, kw, vw = _sink_row(rng, 32, 256, 40, 4)
+        q = rand_bf16(rng, 128) * rng.uniform(0.5, 3)
+        sm = 1 / math.sqrt(128)
+        split = [0, 64, 128][trial % 3]
+        kw_ = dict(sm_scale=sm, tau=0.02, sink_k=ks, sink_v=vs, hist_start=32, split_tokens=split)
+        _, hot_s, s_hist = O.decode_head(q, qh, kw, vw, **kw_)
+        _, hot_n, _ = O.decode_head(q, qh, kw, vw, sink_seed=False, **kw_)
+        assert np.all(hot_s <= hot_n)
+        row_max = max(s_hist.max(), sm * (ks @ q).max(), sm * (kw @ q).max())
+        assert np.all(np.exp(s_hist[~hot_s] - row_max) < 0.02)
