@@ -11,7 +11,11 @@
  *     plane of every token and the low plane only for tokens whose weight reaches tau times
  *     a running maximum seeded by m0 (section 3.3 C3, "Read-time V precision").
  *   - One launch per cell reads its history pages through a per-cell descriptor built at plan
- *     load; split partials merge by log-sum-exp (section 3.4, "One launch per cell").
+ *     load; split partials merge by log-sum-exp (section 3.4, "The unified kernel").
+ *   - Optionally a sink (the first 32 tokens) and a recent window stay exact bf16; a 32-token
+ *     page is quantized when it leaves the window, and the sink's largest score seeds the
+ *     running maximum of the history (section 2.3, "Measuring KV damage"; section 3.2;
+ *     section 3.4, "The unified kernel").
  *   - KIVI-style quantization (section 5.1, "Baselines"): keys per channel over a 32-token
  *     page, values per token over groups of channels, asymmetric, fp16 scale and zero point.
  *
@@ -66,13 +70,19 @@ typedef struct {
   int32_t max_batch;         /* requests per call, at most */
   int32_t max_pages_per_seq; /* page-table row capacity; context <= this * page_tokens */
   int32_t tail_tokens;       /* exact bf16 ring per (cell, request) for tokens not yet
-                                quantized: 32..1024, a multiple of 32 (64 recommended) */
+                                quantized: 32..1024, a multiple of 32 (64 recommended);
+                                with a window, at least window_tokens + 64 */
   int32_t max_splits;        /* split-K partials per row the workspace holds (>= 1) */
+  int32_t sink_tokens;       /* 0 or 32: the first sink_tokens tokens of every request stay
+                                exact bf16 and are never quantized */
+  int32_t window_tokens;     /* 0, or a multiple of 32: a 32-token group past the sink is
+                                quantized only once none of its tokens is among the last
+                                window_tokens positions (0: as soon as it is complete) */
   int32_t reserved;          /* set to 0 */
   int64_t num_pages;         /* physical pages in each own-storage cell's pool */
 } loopkv_shape;
 
-/* Sizes, in bytes. The arena is: metadata | workspace | tails | pools. */
+/* Sizes, in bytes. The arena is: metadata | workspace | tails | sinks | pools. */
 typedef struct {
   uint64_t arena_bytes;      /* total device bytes loopkv_plan_load needs */
   uint64_t pool_bytes;       /* page pools of all own-storage cells */
@@ -86,6 +96,7 @@ typedef struct {
   double stored_bytes_per_token;
   double read_bytes_per_token_hi_only;
   double read_bytes_per_token_all_hot;
+  uint64_t sink_bytes;       /* bf16 sinks of all cells (REUSE cells keep their own) */
 } loopkv_bytes;
 
 /* Per-call decode options. */
@@ -106,7 +117,11 @@ typedef struct {
   unsigned long long* stats_dev; /* optional [4] counters, accumulated (not reset):
                                  [0] history (token, head) pairs read, [1] of those, pairs
                                  whose low plane was read, [2] pairs read from INT4 pools,
-                                 [3] tail (token, head) pairs. NULL to skip. */
+                                 [3] exact (token, head) pairs: sink, window and tail.
+                                 NULL to skip. */
+  int32_t no_sink_seed;       /* 0: with a sink, the running maximum starts at the larger of
+                                 the seed and the sink's largest score (section 3.4); 1: at the
+                                 seed alone */
 } loopkv_decode_opts;
 
 /* Device view of one cell, for inspection by callers and tests. */
@@ -120,8 +135,10 @@ typedef struct {
   void* own_pool_dev;         /* pool this cell writes; NULL for REUSE */
   void* tail_k_dev;           /* bf16 [max_batch, tail_tokens, H, D] ring, slot = pos % tail */
   void* tail_v_dev;
-  int32_t* qgroups_dev;       /* int32 [max_batch]: 32-token groups quantized so far (own
-                                 storage only; a REUSE cell reads its source's) */
+  int32_t* qgroups_dev;       /* int32 [max_batch]: end of the quantized history in 32-token
+                                 groups (own storage only; a REUSE cell reads its source's) */
+  void* sink_k_dev;           /* bf16 [max_batch, sink_tokens, H, D] exact sink; NULL without */
+  void* sink_v_dev;
 } loopkv_cell_info;
 
 /* Sizes of the arena for `shape` and `plan` (num_loops * num_layers codes), and the
@@ -149,13 +166,16 @@ loopkv_status loopkv_plan_free(loopkv_plan plan);
  *   page_table_dev: int32 [batch, page_table_stride], logical page -> physical page id in
  *   [0, num_pages); one table serves every cell.
  * With m = the request's appended count, its last min(m, tail_tokens) tokens enter the
- * cell's bf16 ring. For an own-storage cell, every 32-token key group the append completes is
- * quantized into the cell's pool (KIVI-style, fp16 scale/zero, INT4 values split into hi/lo
- * planes) and the cell's quantized-group counter becomes floor((seq_len + m) / 32). A REUSE
- * cell only fills its ring: its history is the final loop's pool, as far as that cell's
- * counter says. n_new == 0 is a no-op. Precondition (device data): the tokens of a group
- * completed by this call that precede it are still in the ring, i.e. every earlier append of
- * the request also ran. */
+ * cell's bf16 ring, and those at positions below sink_tokens also enter its sink. With
+ * n = seq_len + m, the quantized history of a request ends at group
+ *   qend(n) = max(sink_tokens / 32, floor((n - window_tokens) / 32))
+ * (groups below sink_tokens / 32 are the sink). For an own-storage cell, every group in
+ * [qend(seq_len), qend(n)) -- the groups this append moves out of the window -- is quantized
+ * into the cell's pool (KIVI-style, fp16 scale/zero, INT4 values split into hi/lo planes) and
+ * the cell's counter becomes qend(n). A REUSE cell only fills its ring and sink: its history
+ * is the final loop's pool, as far as that cell's counter says. n_new == 0 is a no-op.
+ * Precondition (device data): the tokens of a group quantized by this call that precede it
+ * are still in the ring, i.e. every earlier append of the request also ran. */
 loopkv_status loopkv_quantize_append(loopkv_plan plan, int32_t layer, int32_t loop,
                                      const void* k_new_dev, const void* v_new_dev,
                                      int32_t batch, int32_t n_new,
@@ -167,12 +187,15 @@ loopkv_status loopkv_quantize_append(loopkv_plan plan, int32_t layer, int32_t lo
 /* Decode attention of cell (layer, loop) for one query token per request.
  *   q_dev: bf16 [batch, num_q_heads, head_dim]; out_dev: fp32 [batch, num_q_heads, head_dim].
  *   seq_lens_dev: int32 [batch], context length including the newest token.
- * History = the first 32*g tokens, g = min(source counter, seq_len / 32), read from the
- * pool the cell's descriptor names; tail = the remaining tokens, read exactly from the
- * cell's own ring (at most tail_tokens of them). Scores are sm_scale * q . k^; softmax over
- * history and tail; history values of an INT4 pool decode at full precision for hot tokens
- * and to the middle of their high-plane bucket for cold ones (section 3.3). A request with
- * seq_len 0 gets zeros. opts may be NULL (tau 0, default scale, no split). */
+ * With n = seq_len, S = sink_tokens and g = max(S / 32, min(source counter, qend(n))):
+ * sink = tokens [0, min(n, S)), read exactly from the cell's own sink; history = tokens
+ * [S, 32*g), read from the pool the cell's descriptor names; tail = tokens [32*g, n), read
+ * exactly from the cell's own ring (at most tail_tokens of them). Scores are
+ * sm_scale * q . k^; softmax over sink, history and tail; history values of an INT4 pool
+ * decode at full precision for hot tokens and to the middle of their high-plane bucket for
+ * cold ones (section 3.3), with the running maximum of each split seeded by the seed joined
+ * with the sink's largest score. A request with seq_len 0 gets zeros. opts may be NULL
+ * (tau 0, default scale, no split). */
 loopkv_status loopkv_decode_attention(loopkv_plan plan, int32_t layer, int32_t loop,
                                       const void* q_dev, int32_t batch,
                                       const int32_t* seq_lens_dev,

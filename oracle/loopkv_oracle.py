@@ -151,7 +151,7 @@ def dequant_values_cold(codes4, s, z):
 
 
 # --------------------------------------------------------------------------------------
-# Read-time V precision mask (§3.3; §3.4 "One launch per cell"; Appendix "Proof of
+# Read-time V precision mask (§3.3; §3.4 "The unified kernel"; Appendix "Proof of
 # Proposition 1")
 # --------------------------------------------------------------------------------------
 def _split_groups(n, start, split_tokens, group):

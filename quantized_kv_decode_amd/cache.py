@@ -63,7 +63,7 @@ class LoopKVCache:
                page_table: torch.Tensor, *, tau: float = 0.0, sm_scale: float = 0.0,
                split_tokens: int = 0, seed: torch.Tensor | None = None,
                fetch_mask: torch.Tensor | None = None, stats: torch.Tensor | None = None,
-               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+               out: torch.Tensor | None = None, sink_seed: bool = True, stream=None) -> torch.Tensor:
         """q: bf16 [B, H, D]; seq_lens: int32 [B] including the new token. Returns fp32 [B, H, D]."""
         assert q.dtype == torch.bfloat16 and q.is_contiguous()
         B = q.shape[0]
@@ -71,7 +71,7 @@ class LoopKVCache:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         opts = L.DecodeOpts(float(tau), float(sm_scale), int(split_tokens),
                             int(fetch_mask.stride(1)) if fetch_mask is not None else 0,
-                            _ptr(seed), _ptr(fetch_mask), _ptr(stats))
+                            _ptr(seed), _ptr(fetch_mask), _ptr(stats), 0 if sink_seed else 1)
         if fetch_mask is not None:
             assert fetch_mask.dtype == torch.uint8 and fetch_mask.stride(2) == 1
             assert fetch_mask.stride(0) == fetch_mask.stride(1) * q.shape[1]
@@ -103,6 +103,19 @@ class LoopKVCache:
             off = p - self.arena.data_ptr()
             views.append(self.arena[off:off + n].view(torch.bfloat16).view(
                 s.max_batch, s.tail_tokens, s.num_kv_heads, s.head_dim))
+        return views[0], views[1]
+
+    def sink(self, layer: int, loop: int) -> tuple[torch.Tensor, torch.Tensor]:
+        """bf16 views [max_batch, sink_tokens, H, D] of the cell's exact sink (K, V)."""
+        info = self.cell_info(layer, loop)
+        s = self.shape
+        assert s.sink_tokens > 0 and info.sink_k_dev
+        n = s.max_batch * s.sink_tokens * s.num_kv_heads * s.head_dim * 2
+        views = []
+        for p in (info.sink_k_dev, info.sink_v_dev):
+            off = p - self.arena.data_ptr()
+            views.append(self.arena[off:off + n].view(torch.bfloat16).view(
+                s.max_batch, s.sink_tokens, s.num_kv_heads, s.head_dim))
         return views[0], views[1]
 
     def qgroups(self, layer: int, loop: int) -> torch.Tensor:

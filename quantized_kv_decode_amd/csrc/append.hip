@@ -1,12 +1,13 @@
 // Quantize-append: the companion step that moves new tokens into a cell's storage.
 //
-// "Loop-Aware KV Cache Compression for Serving Looped Transformers": a 32-token page is
-// quantized into its cell's pool when it leaves the exact window (section 2.3; section 4,
-// "vLLM integration"); KIVI-style asymmetric quantization, keys per channel over the page,
-// values per token over channel groups (section 5.1, "Baselines"); an INT4 cell stores its
-// value codes as a high and a low 2-bit plane (section 3.3, "Bit-plane V layout"). Here a
-// group is quantized by the append that completes it, and the newest tokens stay exact in
-// a per-(cell, request) bf16 ring until then.
+// "Loop-Aware KV Cache Compression for Serving Looped Transformers": the sink stays exact,
+// and a 32-token page is quantized into its cell's pool when it leaves the exact window
+// (section 2.3, "Measuring KV damage"; section 4); KIVI-style asymmetric quantization, keys
+// per channel over the page, values per token over channel groups (section 5.1); an INT4 cell
+// stores its value codes as a high and a low 2-bit plane (section 3.3, "Bit-plane V layout").
+// Here a group is quantized by the append that moves it out of the window (with no window:
+// the append that completes it); until then its tokens stay exact in a per-(cell, request)
+// bf16 ring, and the sink's tokens are also kept in a bf16 sink of their own.
 //
 // Rounding (bit-exact by construction): scale = fp16_rne((max - min) / (2^b - 1)) and
 // zero = fp16_rne(min), each rounded once from a double; code = clamp(floor((x - zero) /
@@ -62,13 +63,13 @@ __device__ __forceinline__ int quant_code(double x, double s, double z, int leve
 
 __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t flag) { atomicOr(err, flag); }
 
-// One workgroup of 128 threads quantizes one completed 32-token key group of one
-// (request, head) into the cell's pool. blockIdx = (group index within this call, head,
+// One workgroup of 128 threads quantizes one 32-token key group that leaves the window, of one
+// (request, head), into the cell's pool. blockIdx = (group index within this call, head,
 // request). With FUSED (calls of at most 32 tokens) the workgroup of group index 0 also copies
-// the call's tokens of its head into the ring and sets the request's quantized-group counter,
+// the call's tokens of its head into the ring (and the sink) and sets the request's counter,
 // which saves the separate ring launch on a decode step: the ring slots it writes (positions
-// old .. old+31) never alias the slots the group reads (positions old-31 .. old-1) in a ring of
-// at least 64 tokens.
+// old .. old+31) never alias the slots the group reads (positions between old-window-31 and
+// old-window+31) in a ring of at least window + 64 tokens.
 // Tokens request b appends in this call: n_new_dev[b] if given (clamped to [0, n_new]).
 __device__ __forceinline__ int appended(const int32_t* n_new_dev, int n_new, int b) {
   if (!n_new_dev) return n_new;
@@ -93,6 +94,8 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
   }
   if (n_new_dev && (n_new_dev[b] < 0 || n_new_dev[b] > n_new) && blockIdx.x == 0 && h == 0 && tid == 0)
     raise_error(g.err, kErrLength);
+  const int64_t q0 = quantized_end(old, g.sink, g.window);   // history end before the call
+  const int64_t q1 = quantized_end(nw, g.sink, g.window);    // and after it
   if (FUSED && blockIdx.x == 0) {
     const int m = (int)(nw - old);
     for (int i = 0; i < m; ++i) {
@@ -100,11 +103,16 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
       const size_t dst = (((size_t)b * g.tail + (old + i) % g.tail) * g.H + h) * g.D + tid;
       d.tail_k[dst] = k_new[src];
       d.tail_v[dst] = v_new[src];
+      if (old + i < g.sink) {
+        const size_t sd = (((size_t)b * g.sink + old + i) * g.H + h) * g.D + tid;
+        d.sink_k[sd] = k_new[src];
+        d.sink_v[sd] = v_new[src];
+      }
     }
-    if (h == 0 && tid == 0) d.own_qgroups[b] = (int)(nw / kGroup);
+    if (h == 0 && tid == 0) d.own_qgroups[b] = (int)q1;
   }
-  const int grp = old / kGroup + (int)blockIdx.x;
-  if ((int64_t)(grp + 1) * kGroup > nw) return;
+  const int grp = (int)q0 + (int)blockIdx.x;
+  if (grp >= q1) return;
 
   __shared__ float ks[kGroup][kHeadDim + 1];
   __shared__ float vs[kGroup][kHeadDim + 1];
@@ -253,6 +261,17 @@ __global__ __launch_bounds__(256) void tail_write_kernel(
   if (old < 0 || nw > cap) return;  // flagged by the quantize kernel
   const int first = m > g.tail ? m - g.tail : 0;
   const int chunks_per_tok = g.H * g.D / 8;  // 16-byte chunks per token
+  // Tokens at positions below the sink length also enter the sink.
+  const int n_sink_new = old < g.sink ? min(m, g.sink - old) : 0;
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < n_sink_new * chunks_per_tok; e += blockDim.x) {
+      const int i = e / chunks_per_tok, r = e % chunks_per_tok;
+      const size_t src = ((size_t)b * n_new + i) * (size_t)(g.H * g.D) + (size_t)r * 8;
+      const size_t dst = ((size_t)b * g.sink + old + i) * (size_t)(g.H * g.D) + (size_t)r * 8;
+      *reinterpret_cast<uint4*>(d.sink_k + dst) = *reinterpret_cast<const uint4*>(k_new + src);
+      *reinterpret_cast<uint4*>(d.sink_v + dst) = *reinterpret_cast<const uint4*>(v_new + src);
+    }
+  }
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)(m - first) * chunks_per_tok;
   if (e < total) {
@@ -264,7 +283,8 @@ __global__ __launch_bounds__(256) void tail_write_kernel(
     *reinterpret_cast<uint4*>(d.tail_k + dst) = *reinterpret_cast<const uint4*>(k_new + src);
     *reinterpret_cast<uint4*>(d.tail_v + dst) = *reinterpret_cast<const uint4*>(v_new + src);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0 && d.own_pool) d.own_qgroups[b] = (int)(nw / kGroup);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && d.own_pool)
+    d.own_qgroups[b] = (int)quantized_end(nw, g.sink, g.window);
 }
 
 }  // namespace
@@ -274,9 +294,9 @@ hipError_t launch_append(const Geom& g, const CellDesc* desc_dev, const CellDesc
                          const int32_t* n_new_dev, const int32_t* seq_lens,
                          const int32_t* page_table, int pt_stride, hipStream_t stream) {
   if (dh.own_pool) {
-    // A call of n tokens completes at most ceil(n / 32) groups of a request.
+    // A call of n tokens moves at most ceil(n / 32) groups of a request out of the window.
     const dim3 grid((unsigned)((n_new + kGroup - 1) / kGroup), (unsigned)g.H, (unsigned)batch);
-    const bool fused = n_new <= kGroup && g.tail >= 2 * kGroup && g.D == 128;
+    const bool fused = n_new <= kGroup && g.tail >= g.window + 2 * kGroup && g.D == 128;
     if (dh.own_bits == 4) {
       if (fused) quantize_group_kernel<4, true><<<grid, 128, 0, stream>>>(g, desc_dev, k_new, v_new, n_new, n_new_dev, seq_lens, page_table, pt_stride);
       else quantize_group_kernel<4, false><<<grid, 128, 0, stream>>>(g, desc_dev, k_new, v_new, n_new, n_new_dev, seq_lens, page_table, pt_stride);

@@ -3,7 +3,7 @@
 // "Loop-Aware KV Cache Compression for Serving Looped Transformers":
 //  - one launch per cell reads history pages through the cell's descriptor, which names the
 //    pool to read (its own, or the final loop's for a reusing cell), the stored bits, and
-//    whether the low value plane is gated (section 3.4, "One launch per cell");
+//    whether the low value plane is gated (section 3.4, "The unified kernel");
 //  - for each page the key codes are read first, so every score of the page is known before
 //    its values are touched; a token is cold when exp(s - m) < tau for a running maximum m
 //    that starts at the seed, and a cold token reads only the high plane and decodes to the
@@ -113,6 +113,15 @@ __device__ __forceinline__ float row_max16(float v) {
   v = dmax(v, dpp_mov<0x140>(v));   // row mirror
   return v;
 }
+// Sum within each 16-lane row, broadcast to the row (the same value in every lane: each step
+// adds the same two partial sums in either order).
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  return v;
+}
 __device__ __forceinline__ float lane_f(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
@@ -200,7 +209,8 @@ struct Smem {
   // (token of pair, page id); the low planes of a round are added in the next one, which reads
   // that round's copies.
   alignas(16) _Float16 wbuf[2][NW][NVG][64];
-  float tail_w[NW][kGroup];               // exact tail weights
+  float tail_w[NW][kGroup];               // exact-token weights of a chunk
+  float sink_max[NW];                     // largest sink score each wave saw
   // Hot tokens of a round, compacted: address of the token's low-plane row, and its value
   // weights / 4 as fp16 (a low code is a quarter of a high-plane step), with a zero after the
   // last so that tokens are read in pairs.
@@ -580,6 +590,145 @@ struct DecodeParams {
   DecodeCall c;
 };
 
+typedef const LKV_GLOBAL uint16_t* gu16;
+
+// Exact (bf16) tokens of one row: the sink and the tail (the window and any tokens not yet
+// quantized), read from the cell's own buffers. Rows of both are [request][slot][head][D].
+struct ExactRow {
+  gu16 sink_k, sink_v, ring_k, ring_v;
+  size_t sink_row0, ring_row0;   // (request, slot 0, head) row index of each buffer
+  int H, ring, sink_n, tail_begin, n_tail;
+};
+
+// 16 bytes (8 channels) of a bf16 row as floats.
+__device__ __forceinline__ void bf16x8(const u32x4 w, float (&x)[8]) {
+  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+}
+
+// Largest score (log2 units) over the sink tokens 8r + j, j = w, w + NW, ..., of one wave: lanes
+// 16r .. 16r + 15 take token row r, eight channels each, and a row sum gives the score.
+template <int NW>
+__device__ __forceinline__ float sink_wave_max(const ExactRow& x, gu16 q, float scale2, int w,
+                                               int lane) {
+  const int cbt = lane & 15, tr = lane >> 4;
+  float qf[8];
+  bf16x8(*reinterpret_cast<const LKV_GLOBAL u32x4*>(q + cbt * 8), qf);
+  float mx = -INFINITY;
+  static_assert(8 % NW == 0, "the waves split the eight tokens of a token row evenly");
+#pragma unroll
+  for (int jj = 0; jj < 8 / NW; ++jj) {
+    const int t = tr * 8 + w + jj * NW;
+    const size_t row = x.sink_row0 + (size_t)min(t, x.sink_n - 1) * x.H;
+    float kf[8];
+    bf16x8(*reinterpret_cast<const LKV_GLOBAL u32x4*>(x.sink_k + row * kHeadDim + cbt * 8), kf);
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaf(qf[i], kf[i], a);
+    a = row_sum16(a);
+    if (t < x.sink_n) mx = dmax(mx, a * scale2);
+  }
+  return dmax(dmax(lane_f(mx, 0), lane_f(mx, 16)), dmax(lane_f(mx, 32), lane_f(mx, 48)));
+}
+
+// Softmax state update for one chunk of exact tokens: chunk ch of the row's exact list (chunk 0
+// is the sink when there is one; the others are 32-token runs of the tail). Keys: lanes
+// 16r .. 16r + 15 hold token row r (tokens 8r .. 8r + 7), eight channels each; values: lanes
+// 8r' .. 8r' + 7 hold tokens 4r' .. 4r' + 3, sixteen channels each, which is the layout of acc.
+// Both halves' loads are issued before the scores are formed.
+template <int NVG, int NW>
+__device__ __forceinline__ void exact_chunk(Smem<NVG, NW>& sm, WaveState<NVG>& st, const ExactRow& x,
+                                            int ch, int has_sink, float scale2, float vs_inv,
+                                            int w, int lane) {
+  const bool is_sink = has_sink && ch == 0;
+  const int cw = ch - has_sink;
+  const int n_c = is_sink ? x.sink_n : min(kGroup, x.n_tail - cw * kGroup);
+  const gu16 kb = is_sink ? x.sink_k : x.ring_k;
+  const gu16 vb = is_sink ? x.sink_v : x.ring_v;
+  const size_t row0 = is_sink ? x.sink_row0 : x.ring_row0;
+  const int ring = is_sink ? (1 << 30) : x.ring;
+  const int slot0 = is_sink ? 0 : (x.tail_begin + cw * kGroup) % x.ring;
+  auto row_of = [&](int t) -> size_t {
+    int slot = slot0 + min(t, n_c - 1);
+    if (slot >= ring) slot -= ring;
+    return row0 + (size_t)slot * x.H;
+  };
+  const int cbt = lane & 15, tr = lane >> 4;
+  const int cbv = lane & 7, tq = lane >> 3;
+  u32x4 kk[8], vv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    kk[j] = *reinterpret_cast<const LKV_GLOBAL u32x4*>(kb + row_of(tr * 8 + j) * kHeadDim + cbt * 8);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const LKV_GLOBAL u32x4* vp =
+        reinterpret_cast<const LKV_GLOBAL u32x4*>(vb + row_of(tq * 4 + j) * kHeadDim + cbv * 16);
+    vv[2 * j] = vp[0];
+    vv[2 * j + 1] = vp[1];
+  }
+  float qf[8];
+  {
+    const float4 a = *reinterpret_cast<const float4*>(&sm.q[cbt * 8]);
+    const float4 b = *reinterpret_cast<const float4*>(&sm.q[cbt * 8 + 4]);
+    qf[0] = a.x; qf[1] = a.y; qf[2] = a.z; qf[3] = a.w;
+    qf[4] = b.x; qf[5] = b.y; qf[6] = b.z; qf[7] = b.w;
+  }
+  float s2[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float kf[8];
+    bf16x8(kk[j], kf);
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaf(qf[i], kf[i], a);
+    a = row_sum16(a);
+    s2[j] = tr * 8 + j < n_c ? a * scale2 : -INFINITY;
+    mx = dmax(mx, s2[j]);
+  }
+  mx = dmax(dmax(lane_f(mx, 0), lane_f(mx, 16)), dmax(lane_f(mx, 32), lane_f(mx, 48)));
+  if (mx > st.M) {
+    if (st.M != -INFINITY) {
+      const float f = fexp2(st.M - mx);
+      st.Lsum *= f;
+      st.W *= f;
+#pragma unroll
+      for (int i = 0; i < NVG; ++i) st.Csum[i] *= f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.acc[i] *= f;
+    }
+    st.M = mx;
+  }
+  float p[8], psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = fexp2(s2[j] - st.M);   // exp2(-inf) = 0 for tokens past the chunk
+    psum += p[j];
+  }
+  if (cbt == 0) {
+    st.Lsum += psum;
+    // odd-channel weight in offset units: p / VS * kWScale * kF
+    float* tw = &sm.tail_w[w][tr * 8];
+    *reinterpret_cast<float4*>(tw) = make_float4(p[0] * vs_inv, p[1] * vs_inv, p[2] * vs_inv, p[3] * vs_inv);
+    *reinterpret_cast<float4*>(tw + 4) = make_float4(p[4] * vs_inv, p[5] * vs_inv, p[6] * vs_inv, p[7] * vs_inv);
+  }
+  wave_lds_sync();
+  const float4 wq = *reinterpret_cast<const float4*>(&sm.tail_w[w][tq * 4]);
+  const float wt[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t v8[8] = {vv[2 * j].x, vv[2 * j].y, vv[2 * j].z, vv[2 * j].w,
+                            vv[2 * j + 1].x, vv[2 * j + 1].y, vv[2 * j + 1].z, vv[2 * j + 1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // exact values, offset-free, in channel c's units (kF[c % 8])
+      st.acc[2 * i] = fmaf(kF[(2 * i) % 8] * wt[j], bf16_lo(v8[i]), st.acc[2 * i]);
+      st.acc[2 * i + 1] = fmaf(kF[(2 * i + 1) % 8] * wt[j], bf16_hi(v8[i]), st.acc[2 * i + 1]);
+    }
+  }
+  wave_lds_sync();
+}
+
 
 constexpr int kMaxOrderBatch = 1024;   // larger batches keep the launch order
 
@@ -649,21 +798,28 @@ void decode_kernel(DecodeParams prm) {
     if (tid == 0 && split == 0 && h == 0) atomicOr(g.err, (uint32_t)kErrLength);
     len = 0;
   }
-  int hist_groups = max(min(as_const((const int32_t*)d->src_qgroups)[b], len / kGroup), 0);
-  int tail_begin = hist_groups * kGroup;
-  int n_tail = len - tail_begin;
+  // Sink [0, sink_n), history groups [hs, he), tail [32 he, len): the history ends where the
+  // source's quantized history ends, and never past this request's own window.
+  const int hs = g.sink / kGroup;
+  const int sink_n = min(len, g.sink);
+  const int he = max(hs, (int)min((int64_t)as_const((const int32_t*)d->src_qgroups)[b],
+                                  quantized_end(len, g.sink, g.window)));
+  int tail_begin = he * kGroup;
+  int n_tail = max(len - tail_begin, 0);
   if (n_tail > g.tail) {
     if (tid == 0 && split == 0 && h == 0) atomicOr(g.err, (uint32_t)kErrTail);
     tail_begin = len - g.tail;
     n_tail = g.tail;
   }
-  int gs = 0, ge = hist_groups;
+  // Splits are runs of split_tokens from token 0; each takes its groups of [hs, he).
+  int gs = hs, ge = he;
   if (c.n_split > 1) {
     const int gps = c.split_tokens / kGroup;
-    gs = min(split * gps, hist_groups);
-    ge = min(gs + gps, hist_groups);
+    gs = min(max(split * gps, hs), he);
+    ge = min(max((split + 1) * gps, hs), he);
   }
-  const bool do_tail = split == c.n_split - 1 && n_tail > 0;
+  const bool last_split = split == c.n_split - 1;
+  const bool do_exact = last_split && (n_tail > 0 || sink_n > 0);
 
   constexpr Layout lay = head_layout(BITS, P, kHeadDim, NVG);
   RowCtx r;
@@ -693,6 +849,27 @@ void decode_kernel(DecodeParams prm) {
   st.Lsum = 0.f;
   st.W = 0.f;
   st.m_run = c.seed ? c.seed[(size_t)b * H + h] * kLog2e : -INFINITY;
+
+  ExactRow ex;
+  ex.sink_k = as_global((const uint16_t*)d->sink_k);
+  ex.sink_v = as_global((const uint16_t*)d->sink_v);
+  ex.ring_k = as_global((const uint16_t*)d->tail_k);
+  ex.ring_v = as_global((const uint16_t*)d->tail_v);
+  ex.sink_row0 = (size_t)b * g.sink * H + h;
+  ex.ring_row0 = (size_t)b * g.tail * H + h;
+  ex.H = H;
+  ex.ring = g.tail;
+  ex.sink_n = sink_n;
+  ex.tail_begin = tail_begin;
+  ex.n_tail = n_tail;
+  // The sink's largest score seeds every split's running maximum (the history of a 2-bit
+  // pool has no low plane to gate, so it needs no seed).
+  const bool sink_seed = k.gated && c.sink_seed && sink_n > 0 && gs < ge;
+  if (sink_seed) {
+    const float mx = sink_wave_max<NW>(ex, as_global(c.q) + ((size_t)b * H + h) * kHeadDim,
+                                       k.scale2, w, lane);
+    if (lane == 0) sm.sink_max[w] = mx;
+  }
   st.hot = 0;
 #pragma unroll
   for (int i = 0; i < NVG; ++i) st.Csum[i] = 0.f;
@@ -702,7 +879,6 @@ void decode_kernel(DecodeParams prm) {
   for (int i = 0; i < 8; ++i) st.lo_word[i] = 0u;
   st.nlo = 0;
 
-  const int cbv = lane & 7, tq8 = lane >> 3;
   const int rounds = (ge - gs + 2 * NW - 1) / (2 * NW);
   const LaneOffs offs = lane_offsets<BITS, NVG, P>(lay, lane);
   PairRegs<BITS, NVG> regs;
@@ -720,80 +896,22 @@ void decode_kernel(DecodeParams prm) {
     pid_cur = pp.tok_pid;
   }
   __syncthreads();
+  if (sink_seed) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) st.m_run = dmax(st.m_run, sm.sink_max[i]);
+  }
 
   for (int rd = 0; rd < rounds; ++rd) round_body<BITS, NVG, P, NW>(sm, st, regs, pid_cur, nid, r, offs, k, rd);
   // Low planes of the last round.
   if (BITS == 4 && rounds > 0) add_prev_lo<NVG, NW>(sm, st, (rounds - 1) & 1, w, lane, k.mk);
 
-  // Exact tail tokens (last split only), in chunks of 32, distributed over the waves.
-  if (do_tail) {
-    const LKV_GLOBAL uint16_t* tail_k = as_global((const uint16_t*)d->tail_k);
-    const LKV_GLOBAL uint16_t* tail_v = as_global((const uint16_t*)d->tail_v);
-    const int n_chunks = (n_tail + kGroup - 1) / kGroup;
-    for (int ch = w; ch < n_chunks; ch += NW) {
-      const int cbt = lane & 15, tqt = lane >> 4;   // keys: 8 channels x 8 tokens
-      for (int j = 0; j < 8; ++j) {
-        const int t = tqt * 8 + j;
-        const int pos = tail_begin + ch * kGroup + t;
-        float part = 0.f;
-        if (ch * kGroup + t < n_tail) {
-          const size_t row = ((size_t)b * g.tail + (pos % g.tail)) * H + h;
-          const u32x4 kv = *reinterpret_cast<const LKV_GLOBAL u32x4*>(tail_k + row * kHeadDim + cbt * 8);
-          const uint32_t kk4[4] = {kv.x, kv.y, kv.z, kv.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            part = fmaf(sm.q[cbt * 8 + 2 * i], bf16_lo(kk4[i]), part);
-            part = fmaf(sm.q[cbt * 8 + 2 * i + 1], bf16_hi(kk4[i]), part);
-          }
-        }
-        sm.red[w][0][cbt][t] = part;
-      }
-      wave_lds_sync();
-      float s2 = -INFINITY;
-      if (lane < kGroup && ch * kGroup + lane < n_tail) {
-        float raw = 0.f;
-#pragma unroll
-        for (int cc = 0; cc < 16; ++cc) raw += sm.red[w][0][cc][lane];
-        s2 = raw * k.scale2;
-      }
-      const float gmx = wave_max(s2);
-      if (gmx > st.M) {
-        if (st.M != -INFINITY) {
-          const float f = fexp2(st.M - gmx);
-          st.Lsum *= f;
-          st.W *= f;
-#pragma unroll
-          for (int i = 0; i < NVG; ++i) st.Csum[i] *= f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) st.acc[i] *= f;
-        }
-        st.M = gmx;
-      }
-      if (lane < kGroup) {
-        const float p = (ch * kGroup + lane < n_tail) ? fexp2(s2 - st.M) : 0.f;
-        st.Lsum += p;
-        // odd-channel weight in offset units: (p / VS) * kWScale / 16; even channels 4x that
-        sm.tail_w[w][lane] = p * (kWScale / VS);
-      }
-      wave_lds_sync();
-      for (int j = 0; j < 4; ++j) {
-        const int t = tq8 * 4 + j;
-        if (ch * kGroup + t >= n_tail) break;
-        const int pos = tail_begin + ch * kGroup + t;
-        const size_t row = ((size_t)b * g.tail + (pos % g.tail)) * H + h;
-        const LKV_GLOBAL u32x4* vp = reinterpret_cast<const LKV_GLOBAL u32x4*>(tail_v + row * kHeadDim + cbv * 16);
-        const u32x4 v0 = vp[0], v1 = vp[1];
-        const uint32_t vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const float wt = sm.tail_w[w][t];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          // exact values, offset-free, in channel c's units (kF[c % 8])
-          st.acc[2 * i] = fmaf(kF[(2 * i) % 8] * wt, bf16_lo(vv[i]), st.acc[2 * i]);
-          st.acc[2 * i + 1] = fmaf(kF[(2 * i + 1) % 8] * wt, bf16_hi(vv[i]), st.acc[2 * i + 1]);
-        }
-      }
-      wave_lds_sync();
-    }
+  // Exact tokens (last split only): the sink, then the tail in chunks of 32, spread over the
+  // row's waves.
+  if (do_exact) {
+    const int has_sink = sink_n > 0 ? 1 : 0;
+    const int n_chunks = has_sink + (n_tail + kGroup - 1) / kGroup;
+    for (int ch = w; ch < n_chunks; ch += NW)
+      exact_chunk<NVG, NW>(sm, st, ex, ch, has_sink, k.scale2, kWScale / VS, w, lane);
   }
 
   // Merge the waves: sum lanes, then combine the NW softmax states.
@@ -857,7 +975,7 @@ void decode_kernel(DecodeParams prm) {
       atomicAdd(&c.stats[1], sm.cnt_hot);
       atomicAdd(&c.stats[2], nh);
     }
-    if (do_tail) atomicAdd(&c.stats[3], (unsigned long long)n_tail);
+    if (do_exact) atomicAdd(&c.stats[3], (unsigned long long)(n_tail + sink_n));
   }
 }
 

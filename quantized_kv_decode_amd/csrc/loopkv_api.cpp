@@ -46,6 +46,11 @@ loopkv_status check_shape(const loopkv_shape* s) {
     return LOOPKV_EINVAL;
   if (s->tail_tokens < 32 || s->tail_tokens > 1024 || s->tail_tokens % 32 != 0)
     return LOOPKV_EINVAL;
+  if (s->sink_tokens != 0 && s->sink_tokens != kGroup) return LOOPKV_EINVAL;
+  if (s->window_tokens < 0 || s->window_tokens % kGroup != 0) return LOOPKV_EINVAL;
+  // the ring holds the window, the partial group behind it, and one group of lag between a
+  // reusing cell and its source
+  if (s->window_tokens > 0 && s->tail_tokens < s->window_tokens + 2 * kGroup) return LOOPKV_EINVAL;
   if (s->num_q_heads != s->num_kv_heads) return LOOPKV_ENOTSUP;
   if (s->head_dim != kHeadDim) return LOOPKV_ENOTSUP;
   if (s->page_tokens != 16 && s->page_tokens != 32) return LOOPKV_ENOTSUP;
@@ -77,8 +82,9 @@ double token_head_bytes(int bits, int D, int nvg, bool with_lo) {
 }
 
 struct ArenaPlan {
-  uint64_t desc_off, counters_off, err_off, partials_off, tails_off, pools_off, total;
+  uint64_t desc_off, counters_off, err_off, partials_off, tails_off, sinks_off, pools_off, total;
   uint64_t tail_bytes_per_cell;  // one of K or V
+  uint64_t sink_bytes_per_cell;  // one of K or V
   std::vector<uint64_t> pool_off;  // per cell; UINT64_MAX for REUSE
   uint64_t pool_bytes;
   loopkv_bytes bytes;
@@ -108,6 +114,13 @@ loopkv_status plan_arena(const loopkv_shape* s, const uint8_t* plan, ArenaPlan* 
   uint64_t tails;
   if (!mul_ok(cells * 2, a->tail_bytes_per_cell, &tails)) return LOOPKV_EINVAL;
   off += tails;
+  a->sinks_off = off;
+  if (!mul_ok((uint64_t)s->max_batch * s->sink_tokens, (uint64_t)H * D * 2, &x))
+    return LOOPKV_EINVAL;
+  a->sink_bytes_per_cell = align_up(x);
+  uint64_t sinks;
+  if (!mul_ok(cells * 2, a->sink_bytes_per_cell, &sinks)) return LOOPKV_EINVAL;
+  off += sinks;
   a->pools_off = off;
   a->pool_off.assign(cells, UINT64_MAX);
   uint64_t pools = 0;
@@ -132,6 +145,7 @@ loopkv_status plan_arena(const loopkv_shape* s, const uint8_t* plan, ArenaPlan* 
   a->bytes.arena_bytes = off;
   a->bytes.pool_bytes = pools;
   a->bytes.tail_bytes = tails;
+  a->bytes.sink_bytes = sinks;
   a->bytes.meta_bytes = meta;
   a->bytes.workspace_bytes = ws;
   a->bytes.stored_bytes_per_token = stored;
@@ -149,6 +163,8 @@ Geom make_geom(const loopkv_plan_s* p) {
   g.v_group = s.v_group;
   g.nvg = s.head_dim / s.v_group;
   g.tail = s.tail_tokens;
+  g.sink = s.sink_tokens;
+  g.window = s.window_tokens;
   g.max_ctx = s.max_pages_per_seq * s.page_tokens;
   g.max_splits = s.max_splits;
   g.num_pages = s.num_pages;
@@ -234,6 +250,10 @@ loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan, v
       d.own_page_bytes = plan[i] == LOOPKV_REUSE ? 0 : d.read_page_bytes;
       d.tail_k = reinterpret_cast<uint16_t*>(base + a.tails_off + (2 * i) * a.tail_bytes_per_cell);
       d.tail_v = reinterpret_cast<uint16_t*>(base + a.tails_off + (2 * i + 1) * a.tail_bytes_per_cell);
+      if (shape->sink_tokens > 0) {
+        d.sink_k = reinterpret_cast<uint16_t*>(base + a.sinks_off + (2 * i) * a.sink_bytes_per_cell);
+        d.sink_v = reinterpret_cast<uint16_t*>(base + a.sinks_off + (2 * i + 1) * a.sink_bytes_per_cell);
+      }
       d.src_qgroups = counters + src * shape->max_batch;
       d.own_qgroups = counters + i * shape->max_batch;
       p->desc[i] = d;
@@ -275,6 +295,8 @@ loopkv_status loopkv_get_cell_info(loopkv_plan p, int32_t layer, int32_t loop,
   out->tail_k_dev = d.tail_k;
   out->tail_v_dev = d.tail_v;
   out->qgroups_dev = d.own_qgroups;
+  out->sink_k_dev = d.sink_k;
+  out->sink_v_dev = d.sink_v;
   return LOOPKV_OK;
 }
 
@@ -347,6 +369,7 @@ loopkv_status loopkv_decode_attention(loopkv_plan p, int32_t layer, int32_t loop
   c.out = out;
   c.partials = p->partials_dev;
   c.order_by_len = 0;   // set by the launcher from the grid size
+  c.sink_seed = o.no_sink_seed ? 0 : 1;
   hipError_t e = launch_decode(g, p->desc[i], c, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LOOPKV_OK : LOOPKV_EHIP;
 }

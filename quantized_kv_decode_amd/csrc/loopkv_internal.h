@@ -51,12 +51,25 @@ __host__ __device__ constexpr Layout head_layout(int bits, int page_tokens, int 
   return l;
 }
 
+// End of the quantized history of a request holding n tokens, in 32-token groups: groups
+// below sink / 32 are the exact sink, and a group past it is quantized once none of its
+// tokens is among the last `window` positions ("Loop-Aware KV Cache Compression for Serving
+// Looped Transformers", section 2.3 "Measuring KV damage", section 3.4 "The unified kernel").
+__host__ __device__ inline int64_t quantized_end(int64_t n, int sink, int window) {
+  const int64_t hs = sink / kGroup;
+  const int64_t x = n - window;
+  const int64_t he = x > 0 ? x / kGroup : 0;
+  return he > hs ? he : hs;
+}
+
 // One descriptor per cell, built by loopkv_plan_load and kept in the arena.
 struct CellDesc {
   uint8_t* read_pool;         // pool read by decode: own, or the final loop's (REUSE)
   uint8_t* own_pool;          // pool written by append; null for REUSE
   uint16_t* tail_k;           // bf16 ring [max_batch][tail_tokens][H][D]
   uint16_t* tail_v;
+  uint16_t* sink_k;           // bf16 [max_batch][sink][H][D]; null without a sink
+  uint16_t* sink_v;
   int32_t* src_qgroups;       // quantized-group counters of the cell whose pool is read
   int32_t* own_qgroups;       // this cell's counters (written by append for own storage)
   int64_t read_page_bytes;
@@ -75,6 +88,8 @@ struct Geom {
   int32_t nvg;           // value groups per head
   int32_t v_group;       // channels per value group
   int32_t tail;          // ring tokens
+  int32_t sink;          // exact sink tokens (0 or 32)
+  int32_t window;        // exact window tokens
   int32_t max_ctx;       // max_pages_per_seq * P
   int32_t max_splits;
   int64_t num_pages;
@@ -106,6 +121,7 @@ struct DecodeCall {
   float* out;
   float* partials;        // [batch, H, max_splits, D + 2]
   int32_t order_by_len;   // launch needs more than one generation: longest requests first
+  int32_t sink_seed;      // seed the running maximum with the sink's largest score
 };
 
 hipError_t launch_decode(const Geom& g, const CellDesc& desc_host, const DecodeCall& c,

@@ -25,7 +25,8 @@ class Shape(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_tokens", ctypes.c_int32),
                 ("v_group", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("tail_tokens", ctypes.c_int32),
-                ("max_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_splits", ctypes.c_int32), ("sink_tokens", ctypes.c_int32),
+                ("window_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("num_pages", ctypes.c_int64)]
 
 
@@ -35,14 +36,15 @@ class Bytes(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_uint64),
                 ("stored_bytes_per_token", ctypes.c_double),
                 ("read_bytes_per_token_hi_only", ctypes.c_double),
-                ("read_bytes_per_token_all_hot", ctypes.c_double)]
+                ("read_bytes_per_token_all_hot", ctypes.c_double),
+                ("sink_bytes", ctypes.c_uint64)]
 
 
 class DecodeOpts(ctypes.Structure):
     _fields_ = [("tau", ctypes.c_float), ("sm_scale", ctypes.c_float),
                 ("split_tokens", ctypes.c_int32), ("mask_stride", ctypes.c_int32),
                 ("seed_dev", ctypes.c_void_p), ("fetch_mask_dev", ctypes.c_void_p),
-                ("stats_dev", ctypes.c_void_p)]
+                ("stats_dev", ctypes.c_void_p), ("no_sink_seed", ctypes.c_int32)]
 
 
 class CellInfo(ctypes.Structure):
@@ -50,7 +52,8 @@ class CellInfo(ctypes.Structure):
                 ("gated", ctypes.c_int32), ("head_block_bytes", ctypes.c_int32),
                 ("page_bytes", ctypes.c_int64), ("read_pool_dev", ctypes.c_void_p),
                 ("own_pool_dev", ctypes.c_void_p), ("tail_k_dev", ctypes.c_void_p),
-                ("tail_v_dev", ctypes.c_void_p), ("qgroups_dev", ctypes.c_void_p)]
+                ("tail_v_dev", ctypes.c_void_p), ("qgroups_dev", ctypes.c_void_p),
+                ("sink_k_dev", ctypes.c_void_p), ("sink_v_dev", ctypes.c_void_p)]
 
 
 SYMBOLS = ["loopkv_cache_bytes", "loopkv_plan_load", "loopkv_plan_free",
@@ -153,6 +156,7 @@ def loopkv_device_errors(handle, stream) -> int:
 
 def make_shape(*, num_layers, num_loops, num_kv_heads=16, head_dim=128, page_tokens=32,
                v_group=128, max_batch, max_pages_per_seq, tail_tokens=64, max_splits=64,
-               num_pages) -> Shape:
+               num_pages, sink_tokens=0, window_tokens=0) -> Shape:
     return Shape(num_layers, num_loops, num_kv_heads, num_kv_heads, head_dim, page_tokens,
-                 v_group, max_batch, max_pages_per_seq, tail_tokens, max_splits, 0, num_pages)
+                 v_group, max_batch, max_pages_per_seq, tail_tokens, max_splits, sink_tokens,
+                 window_tokens, 0, num_pages)

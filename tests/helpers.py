@@ -46,11 +46,15 @@ class Workload:
     appended through the library; the oracle sees the same bf16 values."""
 
     def __init__(self, plan, *, batch, lens, page_tokens=32, v_group=128, heads=16, seed=0,
-                 tail_tokens=64, max_splits=64, shuffle=True, heavy_tail=False, stride_extra=0):
+                 tail_tokens=None, max_splits=64, shuffle=True, heavy_tail=False, stride_extra=0,
+                 sink_tokens=0, window_tokens=0):
         self.plan = np.asarray(plan, np.uint8)
         T, Lr = self.plan.shape
         self.T, self.L, self.B, self.H, self.D = T, Lr, batch, heads, 128
         self.P, self.v_group, self.seed = page_tokens, v_group, seed
+        self.S, self.W = sink_tokens, window_tokens
+        if tail_tokens is None:
+            tail_tokens = 64 if window_tokens == 0 else window_tokens + 64
         self.lens = np.asarray(lens, np.int32)
         self.nmax = max(int(self.lens.max()) if len(self.lens) else 0, 1)
         ptab, npages = synth.page_table(self.lens, page_tokens, seed + 17, shuffle=shuffle)
@@ -61,7 +65,8 @@ class Workload:
         self.num_pages = max(npages, 1)
         self.shape = L.make_shape(num_layers=Lr, num_loops=T, num_kv_heads=heads, page_tokens=page_tokens,
                                   v_group=v_group, max_batch=batch, max_pages_per_seq=stride,
-                                  tail_tokens=tail_tokens, max_splits=max_splits, num_pages=self.num_pages)
+                                  tail_tokens=tail_tokens, max_splits=max_splits, num_pages=self.num_pages,
+                                  sink_tokens=sink_tokens, window_tokens=window_tokens)
         self.cache = LoopKVCache(self.shape, self.plan, zero_arena=True)
         self.page_table = torch.as_tensor(pt).cuda()
         self.k, self.v = {}, {}
@@ -102,31 +107,75 @@ class Workload:
         return torch.as_tensor(self.done[t, l].astype(np.int32)).cuda()
 
     # Oracle views ------------------------------------------------------------------------
+    def qend(self, n):
+        """End of the quantized history (in tokens) of a request holding n tokens."""
+        return O.near_far_split(int(n), self.S, self.W)[2]
+
     def hist(self, t, l):
-        """History tokens decode reads for cell (t, l): the source's whole quantized groups,
-        at most the cell's own length."""
-        src = self.source(t, l)
-        return np.minimum(self.done[src] // 32, self.done[t, l] // 32) * 32
+        """End (in tokens) of the history decode reads for cell (t, l): the source's quantized
+        history, never past the cell's own window. The history starts at the sink length."""
+        st, sl = self.source(t, l)
+        return np.array([min(self.qend(self.done[st, sl][b]), self.qend(self.done[t, l][b]))
+                         for b in range(self.B)], np.int64)
 
     def quant(self, t, l, hist=None):
-        """Oracle QuantHead per (b, h) of storage cell (t, l): its first hist[b] tokens
-        (default: all whole groups appended so far)."""
+        """Oracle QuantHead per (b, h) of storage cell (t, l): its tokens [S, hist[b])
+        (default: everything its own appends have quantized so far)."""
         bits = int(self.plan[t, l])
         if hist is None:
-            hist = (self.done[t, l] // 32) * 32
+            hist = np.array([self.qend(n) for n in self.done[t, l]], np.int64)
         k64, v64 = to64(self.k[t, l]), to64(self.v[t, l])
-        return [[O.quantize_head(k64[b, :hist[b], h], v64[b, :hist[b], h], bits, self.v_group)
+        S = self.S
+        return [[O.quantize_head(k64[b, S:max(hist[b], S), h], v64[b, S:max(hist[b], S), h], bits,
+                                 self.v_group)
                  for h in range(self.H)] for b in range(self.B)]
 
-    def oracle_decode(self, t, l, q, *, tau, split_tokens=0, m0=None, sm_scale=None):
-        """The oracle's decode of cell (t, l) after the appends so far: history from the source
-        cell's quantized groups, tail = the cell's own remaining exact tokens."""
+    def oracle_decode(self, t, l, q, *, tau, split_tokens=0, m0=None, sm_scale=None, sink_seed=True):
+        """The oracle's decode of cell (t, l) after the appends so far: the cell's own sink, history
+        from the source cell's quantized groups, tail = the cell's own remaining exact tokens.
+        Returns (out [B, H, D], hot[b][h])."""
         st, sl = self.source(t, l)
         hist = self.hist(t, l)
         qh = self.quant(st, sl, hist)
         done = self.done[t, l]
         k64, v64 = to64(self.k[t, l]), to64(self.v[t, l])
-        tk = [k64[b, hist[b]:done[b]] for b in range(self.B)]
-        tv = [v64[b, hist[b]:done[b]] for b in range(self.B)]
-        return O.decode_cell(to64(q), qh, tk, tv, tau=tau, split_tokens=split_tokens, m0=m0,
-                             sm_scale=sm_scale)
+        q64 = to64(q)
+        sm = 1.0 / np.sqrt(self.D) if sm_scale is None else sm_scale
+        out = np.zeros((self.B, self.H, self.D))
+        hot = [[None] * self.H for _ in range(self.B)]
+        for b in range(self.B):
+            se = min(int(done[b]), self.S)
+            he = max(int(hist[b]), self.S) if done[b] > 0 else 0
+            for h in range(self.H):
+                seed = -np.inf if m0 is None else float(m0[b, h])
+                out[b, h], hot[b][h], _ = O.decode_head(
+                    q64[b, h], qh[b][h], k64[b, he:done[b], h], v64[b, he:done[b], h], sm_scale=sm,
+                    tau=tau, m0=seed, split_tokens=split_tokens, sink_k=k64[b, :se, h],
+                    sink_v=v64[b, :se, h], hist_start=self.S, sink_seed=sink_seed)
+        return out, hot
+
+    def check_masks(self, mask, hot, t, l, q, tau, split, m0=None, sink_seed=True):
+        """Fetch masks of an INT4-read cell against the oracle's, except near-tau ties."""
+        st, sl = self.source(t, l)
+        if self.plan[st, sl] != L.INT4:
+            return 0
+        hist = self.hist(t, l)
+        qh = self.quant(st, sl, hist)
+        mk = mask.cpu().numpy()
+        q64 = to64(q)
+        k64 = to64(self.k[t, l])
+        ties = 0
+        for b in range(self.B):
+            for h in range(self.H):
+                n = qh[b][h].k_codes.shape[0]
+                if n == 0:
+                    continue
+                kh = O.dequant_keys(qh[b][h].k_codes, qh[b][h].k_s, qh[b][h].k_z)
+                s = (kh @ q64[b, h]) / np.sqrt(128.0)
+                seed = -np.inf if m0 is None else float(m0[b, h])
+                se = min(int(self.done[t, l][b]), self.S)
+                if sink_seed and se > 0:
+                    seed = max(seed, float((k64[b, :se, h] @ q64[b, h]).max() / np.sqrt(128.0)))
+                tie = O.tie_mask(s, seed, tau, split, start=self.S)
+                ties += check_mask(mk[b, h, self.S:], hot[b][h], tie, f"mask b={b} h={h} tau={tau}")
+        return ties

@@ -74,12 +74,23 @@ def test_arena_accounting():
     assert b.pool_bytes == sum((p + 255) // 256 * 256 for p in pools)
     assert b.tail_bytes == 6 * 2 * ((3 * 64 * 16 * 128 * 2 + 255) // 256 * 256)
     assert b.arena_bytes == b.meta_bytes + b.workspace_bytes + b.tail_bytes + b.pool_bytes
+    assert b.sink_bytes == 0
+    # a 32-token sink per (cell, request), kept by reusing cells too; a window widens the ring
+    s = shape(num_layers=2, num_loops=3, num_pages=10, page_tokens=16, max_batch=3,
+              sink_tokens=32, window_tokens=256, tail_tokens=320)
+    b2 = L.loopkv_cache_bytes(s, plan)
+    assert b2.sink_bytes == 6 * 2 * ((3 * 32 * 16 * 128 * 2 + 255) // 256 * 256)
+    assert b2.tail_bytes == 6 * 2 * ((3 * 320 * 16 * 128 * 2 + 255) // 256 * 256)
+    assert b2.arena_bytes == b2.meta_bytes + b2.workspace_bytes + b2.tail_bytes + b2.sink_bytes + b2.pool_bytes
+    assert b2.pool_bytes == b.pool_bytes
 
 
 @pytest.mark.parametrize("bad,status", [
     (dict(head_dim=64), L.ENOTSUP), (dict(page_tokens=8), L.ENOTSUP), (dict(v_group=16), L.ENOTSUP),
     (dict(tail_tokens=48), L.EINVAL), (dict(tail_tokens=0), L.EINVAL), (dict(max_batch=0), L.EINVAL),
     (dict(num_pages=0), L.EINVAL), (dict(max_splits=0), L.EINVAL), (dict(num_layers=0), L.EINVAL),
+    (dict(sink_tokens=16), L.EINVAL), (dict(sink_tokens=64), L.EINVAL), (dict(window_tokens=100), L.EINVAL),
+    (dict(window_tokens=-32), L.EINVAL), (dict(window_tokens=256, tail_tokens=288), L.EINVAL),
 ])
 def test_bad_shapes(bad, status):
     s = shape(**bad)

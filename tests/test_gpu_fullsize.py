@@ -9,7 +9,8 @@ rows against the fp64 oracle, computed row by row from the same generated K/V:
 Shapes: the 96-cell 8K batch-64 cache (32-token pages), the paged serving batch (128 requests of
 1K..16K tokens, 16-token pages in a shuffled table, one appended token per request per cell
 before the decode), and the long-context shape (batch 16, 32K tokens, heavy-tailed keys,
-8K-token splits merged by log-sum-exp)."""
+8K-token splits merged by log-sum-exp), and the 8K batch-64 shape again with a 32-token sink and a
+256-token window kept exact."""
 import math
 
 import numpy as np
@@ -27,7 +28,7 @@ pytestmark = pytest.mark.gpu
 PLAN = np.array([[4], [2], [0], [4]], np.uint8)   # loop 3 reuses the final loop's KV
 
 
-def _run_case(name, *, B, lens, P, split, heavy, seed, rows_per_cell, append_one):
+def _run_case(name, *, B, lens, P, split, heavy, seed, rows_per_cell, append_one, S=0, W=0):
     H, D, tau = 16, 128, 0.01
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens, np.int64)
@@ -36,8 +37,9 @@ def _run_case(name, *, B, lens, P, split, heavy, seed, rows_per_cell, append_one
     pt = torch.as_tensor(pt_np).cuda()
     max_splits = max(1, int(pt_np.shape[1] * P // split)) if split else 1
     shape = L.make_shape(num_layers=1, num_loops=4, num_kv_heads=H, page_tokens=P, v_group=128,
-                         max_batch=B, max_pages_per_seq=pt_np.shape[1], tail_tokens=64,
-                         max_splits=max_splits, num_pages=npages)
+                         max_batch=B, max_pages_per_seq=pt_np.shape[1],
+                         tail_tokens=64 if W == 0 else W + 64, max_splits=max_splits,
+                         num_pages=npages, sink_tokens=S, window_tokens=W)
     cache = LoopKVCache(shape, PLAN, zero_arena=True)
     sample = [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(rows_per_cell)]
     chunk = 4096
@@ -104,17 +106,20 @@ def _run_case(name, *, B, lens, P, split, heavy, seed, rows_per_cell, append_one
         errs, refmax, ties = 0.0, 0.0, 0
         for (b, h) in sample:
             n = int(lens[b])
-            hist = (n // 32) * 32   # every whole group is quantized; the rest is the exact tail
+            # sink [0, se), quantized history [S, he), exact tail [he, n)
+            se, _, he = O.near_far_split(n, S, W)
             ks, vs = kv_rows[src, b, h]
-            qh = O.quantize_head(ks[:hist], vs[:hist], bits, 128)
+            qh = O.quantize_head(ks[S:he], vs[S:he], bits, 128)
             kt, vt = kv_rows[t, b, h]
-            ref, hot, s = O.decode_head(q64[b, h], qh, kt[hist:n], vt[hist:n], sm_scale=1 / math.sqrt(D),
-                                        tau=tau, split_tokens=split)
+            ref, hot, s = O.decode_head(q64[b, h], qh, kt[he:n], vt[he:n], sm_scale=1 / math.sqrt(D),
+                                        tau=tau, split_tokens=split, sink_k=kt[:se], sink_v=vt[:se],
+                                        hist_start=S)
             errs = max(errs, float(np.abs(out[b, h] - ref).max()))
             refmax = max(refmax, float(np.abs(ref).max()))
             if bits == 4:
-                tie = O.tie_mask(s, -math.inf, tau, split)
-                ties += check_mask(mk[b, h], hot, tie, f"[{name}] loop {t} b={b} h={h}")
+                m0 = float((kt[:se] @ q64[b, h]).max()) / math.sqrt(D) if se else -math.inf
+                tie = O.tie_mask(s, m0, tau, split, start=S)
+                ties += check_mask(mk[b, h, S:], hot, tie, f"[{name}] loop {t} b={b} h={h}")
         log(f"[{name}] loop {t}: max err {errs:.3e}, max |ref| {refmax:.3e}, ties {ties}")
         assert errs <= OUT_RTOL * refmax, f"[{name}] loop {t}: {errs:.3e} > {OUT_RTOL} * {refmax:.3e}"
     assert cache.device_errors() == 0
@@ -138,3 +143,10 @@ def test_fullsize_long_context_splits():
     """Batch 16, 32768 tokens, heavy-tailed key outliers, 8192-token splits."""
     _run_case("b16-ctx32k", B=16, lens=[32768] * 16, P=32, split=8192, heavy=True, seed=303,
               rows_per_cell=4, append_one=False)
+
+
+def test_fullsize_ouro14b_b64_ctx8k_sink_window():
+    """The benchmark's per-cell shape in the paper's serving setting: a 32-token sink and a
+    256-token window stay exact, the 7904 tokens between are quantized history."""
+    _run_case("b64-ctx8k-sink-window", B=64, lens=[8192] * 64, P=32, split=0, heavy=False, seed=304,
+              rows_per_cell=8, append_one=False, S=32, W=256)

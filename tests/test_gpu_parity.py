@@ -19,28 +19,6 @@ def _mask_buf(w):
     return torch.full((w.B, w.H, w.page_table_np.shape[1] * w.P), 0xEE, dtype=torch.uint8, device="cuda")
 
 
-def _check_masks(w, mask, hot, t, l, q, tau, split, m0=None):
-    st, sl = w.source(t, l)
-    if w.plan[st, sl] != L.INT4:
-        return 0
-    hist = w.hist(t, l)
-    qh = w.quant(st, sl, hist)
-    mk = mask.cpu().numpy()
-    q64 = to64(q)
-    ties = 0
-    for b in range(w.B):
-        for h in range(w.H):
-            n = int(hist[b])
-            if n == 0:
-                continue
-            kh = O.dequant_keys(qh[b][h].k_codes, qh[b][h].k_s, qh[b][h].k_z)
-            s = (kh @ q64[b, h]) / np.sqrt(128.0)
-            seed = -np.inf if m0 is None else float(m0[b, h])
-            tie = O.tie_mask(s, seed, tau, split)
-            ties += check_mask(mk[b, h], hot[b][h], tie, f"mask b={b} h={h} tau={tau}")
-    return ties
-
-
 @pytest.mark.parametrize("bits", [4, 2])
 @pytest.mark.parametrize("P", [32, 16])
 @pytest.mark.parametrize("v_group", [128, 32])
@@ -94,7 +72,7 @@ def test_decode_single_cell_int4():
                              w.page_table, tau=0.01, split_tokens=split, fetch_mask=mask)
         ref, hot = w.oracle_decode(0, 0, q, tau=0.01, split_tokens=split)
         check_out(out, ref, f"split={split}")
-        _check_masks(w, mask, hot, 0, 0, q, 0.01, split)
+        w.check_masks(mask, hot, 0, 0, q, 0.01, split)
         assert not all(h.all() for h in hot[0]) and any(h.any() for h in hot[0])
 
 
@@ -114,7 +92,7 @@ def test_decode_one_layer_four_loops(variant):
             out = w.cache.decode(0, t, q.cuda(), seq, w.page_table, tau=tau, split_tokens=1024, fetch_mask=mask)
             ref, hot = w.oracle_decode(t, 0, q, tau=tau, split_tokens=1024)
             check_out(out, ref, f"loop {t} tau {tau}")
-            _check_masks(w, mask, hot, t, 0, q, tau, 1024)
+            w.check_masks(mask, hot, t, 0, q, tau, 1024)
             log(f"  loop {t} tau {tau} ok")
     assert w.cache.device_errors() == 0
 
@@ -141,7 +119,7 @@ def test_decode_steps_with_tails_ragged_paged():
                                      seed=seed_dev, fetch_mask=mask)
                 ref, hot = w.oracle_decode(t, l, q, tau=0.02, m0=m0)
                 check_out(out, ref, f"step {step} cell ({t},{l})")
-                _check_masks(w, mask, hot, t, l, q, 0.02, 0, m0)
+                w.check_masks(mask, hot, t, l, q, 0.02, 0, m0)
         log(f"  step {step} ok")
     assert w.cache.device_errors() == 0
 
