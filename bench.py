@@ -35,6 +35,9 @@ WORKLOADS = {
     "one-layer-4loops-b8-ctx4k": (1, 4, 8, 4096, None, None, 1024, False),
     "single-cell-b1-ctx256": (1, 1, 1, 256, "single", None, 64, False),
 }
+# The same caches in the paper's serving setting: a 32-token sink and a 256-token window stay
+# exact bf16 (read as 512 bytes per (token, head)), the groups between them are quantized history.
+NEAR = {"ouro1.4b-96cells-b64-ctx8k-sink32-win256": ("ouro1.4b-96cells-b64-ctx8k", 32, 256)}
 # Workloads small enough to stay in the caches: flushed between timed steps.
 FLUSHED = {"one-layer-4loops-b8-ctx4k", "single-cell-b1-ctx256"}
 # The paged serving batch: the 96-cell plan, 128 requests of uniform 1K..16K tokens in 16-token
@@ -59,7 +62,8 @@ def build_cache(name, seed, tau, plan_name="seeded", v_group=128):
     from quantized_kv_decode_amd import synth
     from quantized_kv_decode_amd.cache import LoopKVCache
 
-    layers, loops, B, N, p4, pr, split, heavy = WORKLOADS[name]
+    base, S, W = NEAR.get(name, (name, 0, 0))
+    layers, loops, B, N, p4, pr, split, heavy = WORKLOADS[base]
     if plan_name != "seeded":
         plan = synth.named_plan(plan_name, layers, loops)
     elif p4 == "single":
@@ -71,8 +75,9 @@ def build_cache(name, seed, tau, plan_name="seeded", v_group=128):
     P = 32
     pages_per_seq = N // P
     shape = L.make_shape(num_layers=layers, num_loops=loops, page_tokens=P, v_group=v_group, max_batch=B,
-                         max_pages_per_seq=pages_per_seq, tail_tokens=64,
-                         max_splits=max(1, N // split) if split else 1, num_pages=B * pages_per_seq)
+                         max_pages_per_seq=pages_per_seq, tail_tokens=64 if W == 0 else W + 64,
+                         max_splits=max(1, N // split) if split else 1, num_pages=B * pages_per_seq,
+                         sink_tokens=S, window_tokens=W)
     cache = LoopKVCache(shape, plan)
     pt_np, _ = synth.page_table([N] * B, P, seed + 1, shuffle=True)
     pt = torch.as_tensor(pt_np).cuda()
@@ -90,7 +95,10 @@ def build_cache(name, seed, tau, plan_name="seeded", v_group=128):
     torch.cuda.synchronize()
     log(f"[bench] filled {int((plan != 0).sum())} own cells in {time.time() - t0:.1f}s; "
         f"arena {cache.bytes.arena_bytes / 2**30:.1f} GiB")
-    return cache, plan, pt, pt_np, dict(layers=layers, loops=loops, B=B, N=N, split=split, heavy=heavy)
+    # quantized history [S, he) and exact tokens (sink and window) per request
+    he = max(S, (N - W) // 32 * 32)
+    return cache, plan, pt, pt_np, dict(layers=layers, loops=loops, B=B, N=N, split=split, heavy=heavy,
+                                        S=S, W=W, n_hist=he - S, n_exact=N - (he - S))
 
 
 def run_step(cache, plan, qs, outs, seq, pt, tau, split, stats=None, events=None, stream=None):
@@ -109,10 +117,11 @@ def run_step(cache, plan, qs, outs, seq, pt, tau, split, stats=None, events=None
             i += 1
 
 
-def algorithmic_bytes(plan, hot_frac, B, N, H=16, n_split=1, v_group=128):
+def algorithmic_bytes(plan, hot_frac, B, N, H=16, n_split=1, v_group=128, n_hist=None, n_exact=0):
     """Bytes one decode step reads/writes by the path's definition: per history (token, head)
-    116 + 32*h bytes for an INT4-read cell and 84 for an INT2-read cell, plus q, out, the
-    page table, and split partials."""
+    116 + 32*h bytes for an INT4-read cell and 84 for an INT2-read cell, 512 per exact bf16
+    (token, head) (sink and window), plus q, out, the page table, and split partials."""
+    n_hist = N if n_hist is None else n_hist
     loops, layers = plan.shape
     total = 0.0
     per_cell = []
@@ -122,7 +131,7 @@ def algorithmic_bytes(plan, hot_frac, B, N, H=16, n_split=1, v_group=128):
             src = plan[loops - 1, l] if plan[t, l] == 0 else plan[t, l]
             vsz = 4 * 128 / v_group - 4          # value scale/zero beyond the 128-channel case
             per_tok = INT4_BASE + vsz + INT4_LO * hot_frac[i] if src == 4 else INT2_BYTES + vsz
-            b = B * N * H * per_tok + B * H * 128 * (2 + 4) + B * (N // 32) * 4
+            b = B * n_hist * H * per_tok + B * n_exact * H * 512 + B * H * 128 * (2 + 4) + B * (N // 32) * 4
             if n_split > 1:
                 b += 2 * B * H * n_split * 130 * 4
             per_cell.append(b)
@@ -186,6 +195,7 @@ def cpu_baseline(cfg, plan, tau, seed, budget_s=12.0):
     from quantized_kv_decode_amd import synth
 
     layers, loops, B, N = cfg["layers"], cfg["loops"], cfg["B"], cfg["N"]
+    S, he = cfg["S"], cfg["S"] + cfg["n_hist"]   # sink [0, S), history [S, he), window [he, N)
     H = 16
     cells = []
     for code in (4, 2, 0):
@@ -202,19 +212,18 @@ def cpu_baseline(cfg, plan, tau, seed, budget_s=12.0):
             k = synth.keys(B, N, H, 128, cs, device="cuda", heavy_tail=cfg["heavy"])[0].double().cpu().numpy()
             v = synth.values(B, N, H, 128, cs, device="cuda")[0].double().cpu().numpy()
             q = synth.queries(B, H, 128, 777 + t * 100 + l, device="cuda").double().cpu().numpy()
-            heads = [O.quantize_head(k[:, h], v[:, h], bits, 128) for h in range(H)]
+            heads = [O.quantize_head(k[S:he, h], v[S:he, h], bits, 128) for h in range(H)]
             pt = np.arange(N // 32)[None, :]
-            pool = O.pack_pool(bits, 32, [heads], pt, N // 32)
+            pool = O.pack_pool(bits, 32, [heads], pt, N // 32, hist_start=S)
             for h in range(H):
-                rows.append((bits, pool, pt[0], h, q[:, h]))
+                rows.append((bits, pool, pt[0], h, q[:, h], k[:, h], v[:, h]))
         timed, done = 0.0, 0
-        e = np.zeros((0, 128))
         while timed < budget_s:
-            bits, pool, ptr, h, qs = rows[done % len(rows)]
+            bits, pool, ptr, h, qs, kk, vv = rows[done % len(rows)]
             t0 = time.perf_counter()
-            qh = O.unpack_pool_head(bits, 32, pool, ptr, N, h, H)
-            O.decode_head(qs[done % B], qh, e, e, sm_scale=1 / math.sqrt(128), tau=tau,
-                          split_tokens=cfg["split"])
+            qh = O.unpack_pool_head(bits, 32, pool, ptr, he - S, h, H, hist_start=S)
+            O.decode_head(qs[done % B], qh, kk[he:], vv[he:], sm_scale=1 / math.sqrt(128), tau=tau,
+                          split_tokens=cfg["split"], sink_k=kk[:S], sink_v=vv[:S], hist_start=S)
             timed += time.perf_counter() - t0
             done += 1
     rows_step = loops * layers * B * H
@@ -405,7 +414,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="ouro1.4b-96cells-b64-ctx8k", choices=sorted(WORKLOADS) + [PAGED],
+    ap.add_argument("--workload", default="ouro1.4b-96cells-b64-ctx8k",
+                    choices=sorted(WORKLOADS) + sorted(NEAR) + [PAGED],
                     help="workloads in FLUSHED evict the caches before every timed step")
     ap.add_argument("--tau", type=float, default=0.01)
     ap.add_argument("--seed", type=int, default=1)
@@ -499,7 +509,8 @@ def main():
         med_ms = graph_ms
 
     n_split = (N + split - 1) // split if split else 1
-    alg_bytes, per_cell_bytes = algorithmic_bytes(plan, hot_frac, B, N, n_split=n_split, v_group=args.v_group)
+    alg_bytes, per_cell_bytes = algorithmic_bytes(plan, hot_frac, B, N, n_split=n_split, v_group=args.v_group,
+                                                  n_hist=cfg["n_hist"], n_exact=cfg["n_exact"])
     # Dominant kernel: the INT4-read decode (own INT4 cells and cells reusing an INT4 source).
     src_bits = np.array([plan[loops - 1, l] if plan[t, l] == 0 else plan[t, l]
                          for t in range(loops) for l in range(layers)])
@@ -544,7 +555,8 @@ def main():
                    "split_tokens": split, "plan_counts": {"int4": int((plan == 4).sum()),
                                                           "int2": int((plan == 2).sum()),
                                                           "reuse": int((plan == 0).sum())},
-                   "page_tokens": 32, "v_group": args.v_group, "plan": args.plan, "plan_seed": args.seed},
+                   "page_tokens": 32, "v_group": args.v_group, "plan": args.plan, "plan_seed": args.seed,
+                   "sink_tokens": cfg["S"], "window_tokens": cfg["W"]},
         "achieved_TBps": round(alg_bytes / (med_ms / 1e3) / 1e12, 3),
         "hot_fraction": round(overall_hot, 4),
         "alg_bytes_per_step": int(alg_bytes),
