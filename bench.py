@@ -64,7 +64,9 @@ def build_cache(name, seed, tau, plan_name="seeded", v_group=128):
 
     base, S, W = NEAR.get(name, (name, 0, 0))
     layers, loops, B, N, p4, pr, split, heavy = WORKLOADS[base]
-    if plan_name != "seeded":
+    if plan_name.startswith("knapsack"):
+        plan = knapsack_plan(plan_name, layers, loops, seed, v_group)
+    elif plan_name != "seeded":
         plan = synth.named_plan(plan_name, layers, loops)
     elif p4 == "single":
         plan = np.array([[4]], np.uint8)
@@ -99,6 +101,27 @@ def build_cache(name, seed, tau, plan_name="seeded", v_group=128):
     he = max(S, (N - W) // 32 * 32)
     return cache, plan, pt, pt_np, dict(layers=layers, loops=loops, B=B, N=N, split=split, heavy=heavy,
                                         S=S, W=W, n_hist=he - S, n_exact=N - (he - S))
+
+
+def knapsack_plan(name, layers, loops, seed, v_group):
+    """A plan from the library's exact planner on a seeded synthetic damage table: read-optimized
+    (damage budget 3x the all-INT4 damage, no storage budget) or memory-optimized (5x, and at most
+    65% of the all-INT4 storage, the ratio of the paper's 156 KiB budget to KIVI-4's 240 KiB)."""
+    from quantized_kv_decode_amd import loopkv as L
+    from quantized_kv_decode_amd import synth
+
+    d = synth.damage_table(layers, loops, seed)
+    d4 = float(np.nansum(d[:, :, 0]))
+    shape = L.make_shape(num_layers=layers, num_loops=loops, v_group=v_group, max_batch=1,
+                         max_pages_per_seq=1, num_pages=1)
+    all4 = L.loopkv_cache_bytes(shape, np.full((loops, layers), 4, np.uint8)).stored_bytes_per_token
+    if name == "knapsack_r":
+        plan, cost = L.loopkv_plan_solve(shape, d, max_damage=3.0 * d4)
+    else:
+        plan, cost = L.loopkv_plan_solve(shape, d, max_damage=5.0 * d4, max_stored_bytes=0.65 * all4)
+    log(f"[bench] {name}: damage {cost.damage:.3f} (all-INT4 {d4:.3f}), stored "
+        f"{cost.stored_bytes_per_token / 1024:.1f} KiB, read {cost.read_bytes_per_token / 1024:.1f} KiB per token")
+    return plan
 
 
 def run_step(cache, plan, qs, outs, seq, pt, tau, split, stats=None, events=None, stream=None):
@@ -423,7 +446,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--plan", default="seeded",
-                    choices=["seeded", "kivi4", "kivi4_loop3_share", "int2_loops123", "loopkv_r", "loopkv_m"],
+                    choices=["seeded", "kivi4", "kivi4_loop3_share", "int2_loops123", "loopkv_r", "loopkv_m",
+                             "knapsack_r", "knapsack_m"],
                     help="the workload's seeded plan, or one of the paper's fixed plans")
     ap.add_argument("--v-group", type=int, default=128, choices=[128, 64, 32])
     ap.add_argument("--calibrate-copy", action="store_true",

@@ -51,7 +51,8 @@ typedef enum {
   LOOPKV_ENOTSUP = 3,   /* a shape this build does not implement */
   LOOPKV_ECAPACITY = 4, /* arena smaller than loopkv_cache_bytes says, or a split count
                            above shape.max_splits */
-  LOOPKV_EHIP = 5       /* a HIP runtime call or kernel launch failed */
+  LOOPKV_EHIP = 5,      /* a HIP runtime call or kernel launch failed */
+  LOOPKV_EINFEASIBLE = 6 /* loopkv_plan_solve: no plan meets the budgets */
 } loopkv_status;
 
 /* Plan codes, one uint8 per cell, indexed plan[loop * num_layers + layer]. */
@@ -212,6 +213,42 @@ loopkv_status loopkv_get_cell_info(loopkv_plan plan, int32_t layer, int32_t loop
  * since the last call, and clears them: 1 = a length out of range, 2 = a page id out of
  * range, 4 = more tail tokens than the ring holds. */
 loopkv_status loopkv_device_errors(loopkv_plan plan, void* stream, uint32_t* flags);
+
+/* Budgets of loopkv_plan_solve. */
+typedef struct {
+  double max_damage;          /* the plan's damage (sum of its cells' damages) must not exceed
+                                 this; a negative value means no damage budget */
+  double max_stored_bytes;    /* stored bytes per token over all cells (loopkv_cache_bytes'
+                                 stored_bytes_per_token) must not exceed this; <= 0: no budget */
+  double hot_fraction;        /* in [0, 1]: share of INT4 low planes counted as read (1: every
+                                 plane, as the paper's read figures count them) */
+} loopkv_plan_budget;
+
+/* What a plan costs: summed damage, stored and read bytes per token (read as counted above). */
+typedef struct {
+  double damage;
+  double stored_bytes_per_token;
+  double read_bytes_per_token;
+} loopkv_plan_cost;
+
+/* The planner (section 1; section 3.1 "Allocation"; Appendix "Layer-only allocation"): chooses
+ * one option per cell -- INT4, INT2, or for loops before the last REUSE of the final loop's KV
+ * at the same layer -- that minimises the bytes read per decode step subject to the damage and
+ * storage budgets, exactly (a multiple-choice knapsack solved by dynamic programming over the
+ * layers). A plan's damage is the sum of its cells' damages (section 2.4: damages add up); a
+ * reusing cell stores nothing and reads its source's bytes. Among plans with the fewest read
+ * bytes it returns one with the least damage, then the least storage.
+ *   shape: num_loops <= 5, num_loops * num_layers <= 256; its heads, head_dim and v_group set
+ *   the byte model (the one loopkv_cache_bytes uses).
+ *   damage: host double [num_loops][num_layers][3], options ordered INT4, INT2, REUSE; the
+ *   final loop's REUSE entry is ignored; the others must be finite.
+ *   plan_out: host uint8 [num_loops * num_layers] (plan[loop * num_layers + layer]).
+ *   cost_out: optional (NULL to skip).
+ * Host only, no HIP call. LOOPKV_EINFEASIBLE when no plan meets the budgets (plan_out is then
+ * untouched); LOOPKV_ENOTSUP beyond the size limits above. */
+loopkv_status loopkv_plan_solve(const loopkv_shape* shape, const double* damage,
+                                const loopkv_plan_budget* budget, uint8_t* plan_out,
+                                loopkv_plan_cost* cost_out);
 
 /* Static string naming a status. */
 const char* loopkv_status_string(loopkv_status status);

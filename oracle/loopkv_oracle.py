@@ -31,6 +31,10 @@ Functions and what pins them (tests/test_oracle_pins.py):
   pack_head_block / unpack          -- round trip, hand-placed single codes
   cache_bytes_ref                   -- the paper's KiB-per-token figures (32-channel
                                       value groups)
+  plan_exhaustive / plan_milp       -- each other (enumeration of every plan vs an integer
+                                      program solved by scipy's HiGHS), closed-form optima
+                                      with no budget and with a zero damage budget,
+                                      monotonicity in the budgets
 No function here is "parity unpinned".
 """
 from __future__ import annotations
@@ -563,3 +567,107 @@ def decode_cell(q, heads_q, tail_k, tail_v, *, tau, sm_scale=None, m0=None, spli
             out[b, h] = o
             hot[b][h] = hm
     return out, hot
+
+
+# --------------------------------------------------------------------------------------
+# Planner (§1; §3 "System Design"; §3.1 "Allocation"; §2.4: single-cell damages add up;
+# §3.2: a shared cell stores nothing and reads the final loop's pages)
+#
+# A plan gives every cell one option: INT4, INT2, or (loops before the last) REUSE of the final
+# loop's KV at the same layer. The planner minimises the bytes read per decode step subject to
+# a damage budget (the sum of the chosen options' single-cell damages) and a storage budget
+# (stored bytes per token). Among plans with the fewest read bytes, the oracle prefers the
+# least damage, then the least storage (reading: the paper names only the objective and the
+# budgets; this order makes the optimum's cost unique).
+# --------------------------------------------------------------------------------------
+PLAN_OPTIONS = (INT4, INT2, REUSE)   # order of the damage table's last axis
+
+
+def plan_cost(plan, damage, num_kv_heads=16, d=128, v_group=128, hot_fraction=1.0):
+    """(damage, stored bytes per token, read bytes per token) of a plan uint8 [T, L].
+    damage: [T, L, 3] per option in PLAN_OPTIONS order. Reads count each INT4-read cell's low
+    plane with weight hot_fraction (1: every plane read)."""
+    plan = np.asarray(plan)
+    T, L = plan.shape
+    dmg = 0.0
+    for t in range(T):
+        for layer in range(L):
+            dmg += float(damage[t, layer, PLAN_OPTIONS.index(int(plan[t, layer]))])
+    b = cache_bytes_ref(plan, num_kv_heads, d, v_group)
+    read = b["read_hi_only"] + hot_fraction * (b["read_all_hot"] - b["read_hi_only"])
+    return dmg, b["stored"], read
+
+
+def _layer_choices(T):
+    """Every option tuple of one layer's T cells (the final loop cannot reuse)."""
+    import itertools
+    opts = [PLAN_OPTIONS] * (T - 1) + [(INT4, INT2)]
+    return list(itertools.product(*opts))
+
+
+def _feasible(cost, max_damage, max_stored):
+    dmg, sto, _ = cost
+    return (max_damage < 0 or dmg <= max_damage) and (max_stored <= 0 or sto <= max_stored)
+
+
+def plan_exhaustive(damage, max_damage=-1.0, max_stored=0.0, num_kv_heads=16, d=128,
+                    v_group=128, hot_fraction=1.0):
+    """Every plan, costed with plan_cost; returns (plan, cost) of the best feasible plan by
+    (reads, damage, storage), or (None, None). For tiny T x L only."""
+    import itertools
+    damage = np.asarray(damage, dtype=np.float64)
+    T, L, _ = damage.shape
+    best, best_cost = None, None
+    for cols in itertools.product(_layer_choices(T), repeat=L):
+        plan = np.array(cols, dtype=np.uint8).T          # [T, L]
+        cost = plan_cost(plan, damage, num_kv_heads, d, v_group, hot_fraction)
+        if not _feasible(cost, max_damage, max_stored):
+            continue
+        key = (round(cost[2], 6), cost[0], cost[1])
+        if best is None or key < best:
+            best, best_cost, best_plan = key, cost, plan
+    return (best_plan, best_cost) if best is not None else (None, None)
+
+
+def plan_milp(damage, max_damage=-1.0, max_stored=0.0, num_kv_heads=16, d=128, v_group=128,
+              hot_fraction=1.0):
+    """The same choice as an integer program: one binary per (layer, option tuple of its
+    cells), exactly one per layer, the budgets as linear constraints; scipy's milp (HiGHS)
+    minimises the reads, then, with the reads fixed, the damage. Returns (plan, cost) or
+    (None, None) when infeasible."""
+    from scipy.optimize import Bounds, LinearConstraint, milp
+    damage = np.asarray(damage, dtype=np.float64)
+    T, L, _ = damage.shape
+    ch = _layer_choices(T)
+    K = len(ch)
+    rd = np.zeros(L * K)
+    st = np.zeros(L * K)
+    dm = np.zeros(L * K)
+    for layer in range(L):
+        for k, opts in enumerate(ch):
+            col = np.array(opts, dtype=np.uint8)[:, None]
+            cd, cs, cr = plan_cost(col, damage[:, layer:layer + 1], num_kv_heads, d, v_group,
+                                   hot_fraction)
+            rd[layer * K + k], st[layer * K + k], dm[layer * K + k] = cr, cs, cd
+    one = np.zeros((L, L * K))
+    for layer in range(L):
+        one[layer, layer * K:(layer + 1) * K] = 1
+    cons = [LinearConstraint(one, 1, 1)]
+    if max_damage >= 0:
+        cons.append(LinearConstraint(dm[None], -np.inf, max_damage))
+    if max_stored > 0:
+        cons.append(LinearConstraint(st[None], -np.inf, max_stored))
+    opt = {"mip_rel_gap": 0.0}
+    ints = np.ones(L * K)
+    r1 = milp(rd, constraints=cons, integrality=ints, bounds=Bounds(0, 1), options=opt)
+    if r1.x is None:
+        return None, None
+    r_best = float(rd @ np.round(r1.x))
+    cons2 = cons + [LinearConstraint(rd[None], -np.inf, r_best + 1e-6 * max(r_best, 1.0))]
+    r2 = milp(dm, constraints=cons2, integrality=ints, bounds=Bounds(0, 1), options=opt)
+    x = np.round(r2.x if r2.x is not None else r1.x)
+    plan = np.zeros((T, L), dtype=np.uint8)
+    for layer in range(L):
+        k = int(np.argmax(x[layer * K:(layer + 1) * K]))
+        plan[:, layer] = ch[k]
+    return plan, plan_cost(plan, damage, num_kv_heads, d, v_group, hot_fraction)

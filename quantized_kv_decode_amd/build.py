@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libloopkv.so")
-SOURCES = ["loopkv_api.cpp", "append.hip", "decode.hip"]
+SOURCES = ["loopkv_api.cpp", "planner.cpp", "append.hip", "decode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 VALU ops are kept out of every kernel.

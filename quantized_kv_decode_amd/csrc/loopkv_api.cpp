@@ -25,18 +25,7 @@ struct loopkv_plan_s {
   int cus = 0;                    // compute units of that device
 };
 
-namespace {
-
-constexpr uint64_t kAlign = 256;
-
-uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-// Multiplies with an overflow check; returns false on overflow.
-bool mul_ok(uint64_t a, uint64_t b, uint64_t* r) {
-  if (a != 0 && b > UINT64_MAX / a) return false;
-  *r = a * b;
-  return true;
-}
+namespace loopkv {
 
 loopkv_status check_shape(const loopkv_shape* s) {
   if (!s) return LOOPKV_EINVAL;
@@ -61,6 +50,29 @@ loopkv_status check_shape(const loopkv_shape* s) {
   return LOOPKV_OK;
 }
 
+// Algorithmic bytes of one (token, head) stored at `bits`: key codes, the token's share of
+// its key group's fp16 (s, z), value codes or planes, value (s, z).
+double token_head_bytes(int bits, int D, int nvg, bool with_lo) {
+  double b = D * bits / 8.0 + 4.0 * D / kGroup + D / 4.0 + 4.0 * nvg;
+  if (bits == 4 && with_lo) b += D / 4.0;
+  return b;
+}
+
+}  // namespace loopkv
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Multiplies with an overflow check; returns false on overflow.
+bool mul_ok(uint64_t a, uint64_t b, uint64_t* r) {
+  if (a != 0 && b > UINT64_MAX / a) return false;
+  *r = a * b;
+  return true;
+}
+
 loopkv_status check_plan(const loopkv_shape* s, const uint8_t* plan) {
   if (!plan) return LOOPKV_EINVAL;
   const int T = s->num_loops, L = s->num_layers;
@@ -71,14 +83,6 @@ loopkv_status check_plan(const loopkv_shape* s, const uint8_t* plan) {
       if (c == LOOPKV_REUSE && t == T - 1) return LOOPKV_EPLAN;
     }
   return LOOPKV_OK;
-}
-
-// Algorithmic bytes of one (token, head) stored at `bits`: key codes, the token's share of
-// its key group's fp16 (s, z), value codes or planes, value (s, z).
-double token_head_bytes(int bits, int D, int nvg, bool with_lo) {
-  double b = D * bits / 8.0 + 4.0 * D / kGroup + D / 4.0 + 4.0 * nvg;
-  if (bits == 4 && with_lo) b += D / 4.0;
-  return b;
 }
 
 struct ArenaPlan {
@@ -189,6 +193,7 @@ const char* loopkv_status_string(loopkv_status st) {
     case LOOPKV_ENOTSUP: return "unsupported shape";
     case LOOPKV_ECAPACITY: return "insufficient capacity";
     case LOOPKV_EHIP: return "HIP runtime error";
+    case LOOPKV_EINFEASIBLE: return "no plan meets the budgets";
   }
   return "unknown status";
 }

@@ -97,6 +97,11 @@ struct Geom {
   int32_t cus;           // compute units of the device
 };
 
+// Host-side checks and the byte model shared by the API and the planner.
+loopkv_status check_shape(const loopkv_shape* s);
+// Algorithmic bytes of one (token, head) stored at `bits` (with_lo: an INT4 cell's low plane).
+double token_head_bytes(int bits, int D, int nvg, bool with_lo);
+
 // Launchers implemented next to their kernels.
 hipError_t launch_append(const Geom& g, const CellDesc* desc_dev, const CellDesc& desc_host,
                          const uint16_t* k_new, const uint16_t* v_new, int batch, int n_new,

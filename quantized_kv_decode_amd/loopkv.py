@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("LOOPKV_LIBRARY") or os.path.join(HERE, "libloopkv.so")
 
 REUSE, INT2, INT4 = 0, 2, 4
-OK, EINVAL, EPLAN, ENOTSUP, ECAPACITY, EHIP = range(6)
+OK, EINVAL, EPLAN, ENOTSUP, ECAPACITY, EHIP, EINFEASIBLE = range(7)
 ERR_LENGTH, ERR_PAGE, ERR_TAIL = 1, 2, 4
 
 
@@ -56,9 +56,19 @@ class CellInfo(ctypes.Structure):
                 ("sink_k_dev", ctypes.c_void_p), ("sink_v_dev", ctypes.c_void_p)]
 
 
+class PlanBudget(ctypes.Structure):
+    _fields_ = [("max_damage", ctypes.c_double), ("max_stored_bytes", ctypes.c_double),
+                ("hot_fraction", ctypes.c_double)]
+
+
+class PlanCost(ctypes.Structure):
+    _fields_ = [("damage", ctypes.c_double), ("stored_bytes_per_token", ctypes.c_double),
+                ("read_bytes_per_token", ctypes.c_double)]
+
+
 SYMBOLS = ["loopkv_cache_bytes", "loopkv_plan_load", "loopkv_plan_free",
            "loopkv_quantize_append", "loopkv_decode_attention", "loopkv_get_cell_info",
-           "loopkv_device_errors", "loopkv_status_string"]
+           "loopkv_device_errors", "loopkv_plan_solve", "loopkv_status_string"]
 
 _lib = None
 
@@ -79,6 +89,8 @@ def lib() -> ctypes.CDLL:
                                               ctypes.POINTER(DecodeOpts), vp, vp]
         L.loopkv_get_cell_info.argtypes = [vp, i32, i32, ctypes.POINTER(CellInfo)]
         L.loopkv_device_errors.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
+        L.loopkv_plan_solve.argtypes = [ctypes.POINTER(Shape), vp, ctypes.POINTER(PlanBudget), vp,
+                                        ctypes.POINTER(PlanCost)]
         L.loopkv_status_string.argtypes = [ctypes.c_int]
         L.loopkv_status_string.restype = ctypes.c_char_p
         for name in SYMBOLS:
@@ -152,6 +164,20 @@ def loopkv_device_errors(handle, stream) -> int:
     v = ctypes.c_uint32()
     _check(lib().loopkv_device_errors(handle, stream, ctypes.byref(v)), "loopkv_device_errors")
     return v.value
+
+
+def loopkv_plan_solve(shape: Shape, damage, max_damage: float = -1.0, max_stored_bytes: float = 0.0,
+                      hot_fraction: float = 1.0):
+    """damage: float64 [num_loops, num_layers, 3] (INT4, INT2, REUSE). Returns (plan uint8
+    [num_loops, num_layers], PlanCost)."""
+    d = np.ascontiguousarray(np.asarray(damage, dtype=np.float64))
+    assert d.shape == (shape.num_loops, shape.num_layers, 3)
+    plan = np.zeros((shape.num_loops, shape.num_layers), np.uint8)
+    cost = PlanCost()
+    b = PlanBudget(float(max_damage), float(max_stored_bytes), float(hot_fraction))
+    _check(lib().loopkv_plan_solve(ctypes.byref(shape), d.ctypes.data, ctypes.byref(b), plan.ctypes.data,
+                                   ctypes.byref(cost)), "loopkv_plan_solve")
+    return plan, cost
 
 
 def make_shape(*, num_layers, num_loops, num_kv_heads=16, head_dim=128, page_tokens=32,

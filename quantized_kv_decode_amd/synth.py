@@ -148,3 +148,27 @@ def page_table(lens_tokens, page_tokens: int, seed: int, stride: int | None = No
         tab[b, :n] = ids[pos:pos + n]
         pos += n
     return tab, total
+
+
+def damage_table(num_layers: int, num_loops: int, seed: int) -> np.ndarray:
+    """A synthetic per-cell damage profile, float64 [num_loops, num_layers, 3] for the options
+    (INT4, INT2, REUSE), shaped like the properties the paper reports for Ouro: a few middle
+    layers are far more sensitive than the rest; 2-bit codes cost about an order of magnitude
+    more than 4-bit ones; reusing the final loop's KV is expensive in the first loop and cheap
+    in the late loops (often cheaper than 2-bit codes in the loop before the last). The final
+    loop's REUSE entry is NaN (it has nothing to reuse). Lognormal noise, seeded."""
+    rng = np.random.default_rng(seed)
+    L, T = num_layers, num_loops
+    pos = (np.arange(L) + 0.5) / L
+    sens = 1.0 + 9.0 * np.exp(-((pos - 0.5) / 0.12) ** 2)          # sensitive middle layers
+    sens *= np.exp(rng.normal(0, 0.4, size=L))
+    d = np.empty((T, L, 3))
+    for t in range(T):
+        loop_w = np.exp(rng.normal(0, 0.2, size=L)) * (1.3 if t == 0 else 1.0)
+        d[t, :, 0] = 0.004 * sens * loop_w * np.exp(rng.normal(0, 0.3, size=L))
+        d[t, :, 1] = d[t, :, 0] * 10.0 * np.exp(rng.normal(0, 0.4, size=L))
+        frac = t / max(T - 1, 1)                                      # 0 first loop .. 1 final
+        share = 3.0 * (1.0 - frac) ** 2 + 0.25
+        d[t, :, 2] = d[t, :, 1] * share * np.exp(rng.normal(0, 0.5, size=L))
+    d[T - 1, :, 2] = np.nan
+    return d

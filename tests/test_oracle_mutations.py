@@ -96,6 +96,22 @@ def _decode_head_sink_dropped(*a, **kw):
     return M.__dict__["_orig_decode_head"](*a, **kw)
 
 
+def _plan_cost_reuse_reads_nothing(plan, damage, num_kv_heads=16, d=128, v_group=128, hot_fraction=1.0):
+    dmg, sto, read = M.__dict__["_orig_plan_cost"](plan, damage, num_kv_heads, d, v_group, hot_fraction)
+    plan = np.asarray(plan)
+    T = plan.shape[0]
+    for t in range(T):
+        for layer in range(plan.shape[1]):
+            if plan[t, layer] == 0:
+                src = int(plan[T - 1, layer])
+                read -= sum(M.token_head_bytes(src, d, v_group).values()) * num_kv_heads
+    return dmg, sto, read
+
+
+def _feasible_ignores_storage(cost, max_damage, max_stored):
+    return max_damage < 0 or cost[0] <= max_damage
+
+
 def _pack_rowmajor(codes, per_word, width):
     p, d = codes.shape
     c = codes.astype(np.uint64).reshape(p, d // per_word, per_word)
@@ -150,6 +166,10 @@ MUTANTS = {
                                           [P.test_dominant_sink_seed_makes_history_cold], []),
     "sink left out of the softmax": ("decode_head", _decode_head_sink_dropped,
                                      [P.test_sink_window_attention_reduces_to_library_sdpa], [4, 0.0]),
+    "a reusing cell reads nothing": ("plan_cost", _plan_cost_reuse_reads_nothing,
+                                     [P.test_planner_closed_form_optima], []),
+    "enumeration ignores the storage budget": ("_feasible", _feasible_ignores_storage,
+                                               [P.test_planner_exhaustive_matches_integer_program], [3, 2]),
 }
 
 
@@ -159,6 +179,7 @@ def test_pins_catch_mutant(name, monkeypatch):
     monkeypatch.setitem(M.__dict__, "_orig_fetch_mask", M.fetch_mask)
     monkeypatch.setitem(M.__dict__, "_orig_token_head_bytes", M.token_head_bytes)
     monkeypatch.setitem(M.__dict__, "_orig_decode_head", M.decode_head)
+    monkeypatch.setitem(M.__dict__, "_orig_plan_cost", M.plan_cost)
     monkeypatch.setattr(M, attr, mutant)
     monkeypatch.setattr(O, attr, mutant, raising=False)
     caught = []

@@ -472,3 +472,70 @@ def test_sink_seed_monotone_and_proposition1():
         assert np.all(hot_s <= hot_n)
         row_max = max(s_hist.max(), sm * (ks @ q).max(), sm * (kw @ q).max())
         assert np.all(np.exp(s_hist[~hot_s] - row_max) < 0.02)
+
+
+# ------------------------------------------------------------------ planner
+def _tiny_damage(rng, T, L):
+    d = rng.lognormal(-3, 1.0, size=(T, L, 3))
+    d[:, :, 1] += d[:, :, 0]          # 2-bit codes cost more than 4-bit ones
+    d[T - 1, :, 2] = np.nan
+    return d
+
+
+@pytest.mark.parametrize("T,L", [(2, 2), (3, 2), (2, 3)])
+def test_planner_exhaustive_matches_integer_program(T, L):
+    """Two independent exact methods -- enumerating every plan, and scipy's MILP solver over
+    one binary per (layer, option tuple) -- agree on the optimum's reads and damage."""
+    rng = np.random.default_rng(100 + 10 * T + L)
+    for trial in range(4):
+        d = _tiny_damage(rng, T, L)
+        d4 = float(d[:, :, 0].sum())
+        all4 = O.plan_cost(np.full((T, L), 4, np.uint8), d)[1]
+        # storage budgets below the all-INT2 plan's (0.57 of all-INT4) force reusing cells
+        md = [-1.0, d4 * rng.uniform(1.2, 4.0), -1.0, d4 * rng.uniform(3.0, 8.0)][trial]
+        ms = [0.0, 0.0, all4 * 0.5, all4 * 0.55][trial]
+        if trial == 3:
+            # a binding storage budget: 2-bit codes are too damaging, so every cell reads 4 bits,
+            # and only reusing cells can bring the storage under 80% of the all-INT4 plan's
+            d[:, :, 0], d[:, :, 1], d[:, :, 2] = 0.01, 1.0, 0.02
+            d[T - 1, :, 2] = np.nan
+            md, ms = 0.5, all4 * 0.8
+        pe, ce = O.plan_exhaustive(d, md, ms)
+        pm, cm = O.plan_milp(d, md, ms)
+        assert (pe is None) == (pm is None)
+        if pe is None:
+            continue
+        assert ce[2] == cm[2] and abs(ce[0] - cm[0]) <= 1e-12 * max(1.0, ce[0])
+        assert (pe[T - 1] != O.REUSE).all()
+
+
+def test_planner_closed_form_optima():
+    """No budget: every cell reads 2-bit bytes (reusing a 2-bit final loop reads the same), so
+    the reads are those of the all-INT2 plan. A zero damage budget with free 4-bit codes forces
+    the all-INT4 plan."""
+    rng = np.random.default_rng(7)
+    T, L = 3, 2
+    d = _tiny_damage(rng, T, L)
+    all2 = np.full((T, L), 2, np.uint8)
+    p, c = O.plan_exhaustive(d)
+    assert c[2] == O.plan_cost(all2, d)[2]
+    assert all(int(p[t, l]) == 2 or (int(p[t, l]) == 0 and int(p[T - 1, l]) == 2)
+               for t in range(T) for l in range(L))
+    d0 = d.copy()
+    d0[:, :, 0] = 0.0
+    p, c = O.plan_exhaustive(d0, max_damage=0.0)
+    assert (p == 4).all() and c[0] == 0.0
+    assert O.plan_milp(d0, max_damage=0.0)[1][2] == O.plan_cost(np.full((T, L), 4, np.uint8), d0)[2]
+
+
+def test_planner_monotone_in_budgets():
+    rng = np.random.default_rng(8)
+    d = _tiny_damage(rng, 3, 2)
+    d4 = float(d[:, :, 0].sum())
+    prev = None
+    for f in [1.0, 1.5, 2.5, 4.0, 8.0]:
+        _, c = O.plan_exhaustive(d, max_damage=d4 * f)
+        assert c is not None
+        if prev is not None:
+            assert c[2] <= prev
+        prev = c[2]
