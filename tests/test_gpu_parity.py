@@ -145,3 +145,22 @@ def test_device_errors_flag_bad_lengths():
     assert w.cache.device_errors() & L.ERR_LENGTH
     assert torch.all(out[1] == 0)
     assert w.cache.device_errors() == 0
+
+
+@pytest.mark.parametrize("v_group", [64, 32])
+def test_decode_value_groups(v_group):
+    """64- and 32-channel value groups (two and four value scales per token and head): plan
+    [4, 2, REUSE, 4], ragged lengths, splits of 0 and 256 tokens, tau in {0, 0.02}."""
+    plan = np.array([[4], [2], [0], [4]], np.uint8)
+    w = Workload(plan, batch=3, lens=[700, 333, 64], v_group=v_group, seed=61 + v_group)
+    w.append_upto(w.lens, chunk=200)
+    for t in range(4):
+        q = synth.queries(3, 16, 128, 300 + t)
+        for tau, split in [(0.0, 0), (0.02, 0), (0.02, 256)]:
+            mask = _mask_buf(w)
+            out = w.cache.decode(0, t, q.cuda(), w.seq_lens(t, 0), w.page_table, tau=tau,
+                                 split_tokens=split, fetch_mask=mask)
+            ref, hot = w.oracle_decode(t, 0, q, tau=tau, split_tokens=split)
+            check_out(out, ref, f"G={v_group} loop {t} tau {tau} split {split}")
+            w.check_masks(mask, hot, t, 0, q, tau, split)
+    assert w.cache.device_errors() == 0
