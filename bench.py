@@ -56,7 +56,7 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def build_cache(name, seed, tau, plan_name="seeded", v_group=128):
+def build_cache(name, seed, tau, plan_name="seeded", v_group=128, shuffle=True):
     import torch
     from quantized_kv_decode_amd import loopkv as L
     from quantized_kv_decode_amd import synth
@@ -81,7 +81,7 @@ def build_cache(name, seed, tau, plan_name="seeded", v_group=128):
                          max_splits=max(1, N // split) if split else 1, num_pages=B * pages_per_seq,
                          sink_tokens=S, window_tokens=W)
     cache = LoopKVCache(shape, plan)
-    pt_np, _ = synth.page_table([N] * B, P, seed + 1, shuffle=True)
+    pt_np, _ = synth.page_table([N] * B, P, seed + 1, shuffle=shuffle)
     pt = torch.as_tensor(pt_np).cuda()
     zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
     t0 = time.time()
@@ -450,6 +450,9 @@ def main():
                              "knapsack_r", "knapsack_m"],
                     help="the workload's seeded plan, or one of the paper's fixed plans")
     ap.add_argument("--v-group", type=int, default=128, choices=[128, 64, 32])
+    ap.add_argument("--pages", default="shuffled", choices=["shuffled", "in-order"],
+                    help="physical page order of each request's pages (the paged serving batch is "
+                         "always shuffled)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -464,7 +467,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == PAGED:
         return run_paged(args)
-    cache, plan, pt, pt_np, cfg = build_cache(args.workload, args.seed, args.tau, args.plan, args.v_group)
+    cache, plan, pt, pt_np, cfg = build_cache(args.workload, args.seed, args.tau, args.plan, args.v_group,
+                                              shuffle=args.pages == "shuffled")
     loops, layers = plan.shape
     B, N, split = cfg["B"], cfg["N"], cfg["split"]
     ncell = loops * layers
@@ -580,7 +584,7 @@ def main():
                                                           "int2": int((plan == 2).sum()),
                                                           "reuse": int((plan == 0).sum())},
                    "page_tokens": 32, "v_group": args.v_group, "plan": args.plan, "plan_seed": args.seed,
-                   "sink_tokens": cfg["S"], "window_tokens": cfg["W"]},
+                   "sink_tokens": cfg["S"], "window_tokens": cfg["W"], "pages": args.pages},
         "achieved_TBps": round(alg_bytes / (med_ms / 1e3) / 1e12, 3),
         "hot_fraction": round(overall_hot, 4),
         "alg_bytes_per_step": int(alg_bytes),
