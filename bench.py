@@ -32,7 +32,7 @@ WORKLOADS = {
     # name: (layers, loops, batch, context, p_int4, p_reuse, split_tokens, heavy_tail)
     "ouro1.4b-96cells-b64-ctx8k": (24, 4, 64, 8192, 0.40, 0.25, 0, False),
     "ouro2.6b-192cells-b16-ctx32k": (48, 4, 16, 32768, 0.30, 0.25, 8192, True),
-    "one-layer-4loops-b8-ctx4k": (1, 4, 8, 4096, None, None, 1024, False),
+    "one-layer-4loops-b8-ctx4k": (1, 4, 8, 4096, None, None, 2048, False),
     "single-cell-b1-ctx256": (1, 1, 1, 256, "single", None, 64, False),
 }
 # The same caches in the paper's serving setting: a 32-token sink and a 256-token window stay
@@ -56,7 +56,7 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def build_cache(name, seed, tau, plan_name="seeded", v_group=128, shuffle=True):
+def build_cache(name, seed, tau, plan_name="seeded", v_group=128, shuffle=True, split_override=None):
     import torch
     from quantized_kv_decode_amd import loopkv as L
     from quantized_kv_decode_amd import synth
@@ -64,6 +64,8 @@ def build_cache(name, seed, tau, plan_name="seeded", v_group=128, shuffle=True):
 
     base, S, W = NEAR.get(name, (name, 0, 0))
     layers, loops, B, N, p4, pr, split, heavy = WORKLOADS[base]
+    if split_override is not None:
+        split = split_override
     if plan_name.startswith("knapsack"):
         plan = knapsack_plan(plan_name, layers, loops, seed, v_group)
     elif plan_name != "seeded":
@@ -450,6 +452,8 @@ def main():
                              "knapsack_r", "knapsack_m"],
                     help="the workload's seeded plan, or one of the paper's fixed plans")
     ap.add_argument("--v-group", type=int, default=128, choices=[128, 64, 32])
+    ap.add_argument("--split", type=int, default=None,
+                    help="split_tokens (a multiple of 32; 0 = one split per row) instead of the workload's")
     ap.add_argument("--pages", default="shuffled", choices=["shuffled", "in-order"],
                     help="physical page order of each request's pages (the paged serving batch is "
                          "always shuffled)")
@@ -468,7 +472,7 @@ def main():
     if args.workload == PAGED:
         return run_paged(args)
     cache, plan, pt, pt_np, cfg = build_cache(args.workload, args.seed, args.tau, args.plan, args.v_group,
-                                              shuffle=args.pages == "shuffled")
+                                              shuffle=args.pages == "shuffled", split_override=args.split)
     loops, layers = plan.shape
     B, N, split = cfg["B"], cfg["N"], cfg["split"]
     ncell = loops * layers
