@@ -96,6 +96,38 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
     raise_error(g.err, kErrLength);
   const int64_t q0 = quantized_end(old, g.sink, g.window);   // history end before the call
   const int64_t q1 = quantized_end(nw, g.sink, g.window);    // and after it
+  const int grp = (int)q0 + (int)blockIdx.x;
+  const bool has_group = grp < q1;
+
+  __shared__ float ks[kGroup][kHeadDim + 1];
+  __shared__ float vs[kGroup][kHeadDim + 1];
+  __shared__ uint8_t kcode[kGroup][kHeadDim];
+  __shared__ uint8_t vcode[kGroup][kHeadDim];
+  __shared__ uint32_t vsz[kGroup][4];
+  __shared__ int64_t page_base[kGroup / 16];
+
+  const int H = g.H, D = g.D;
+  // The group's page ids and its 32 tokens are requested first, so their latencies overlap
+  // each other and the ring copy below. Tokens before `old` come from the ring, later ones from
+  // this call's input; each wave reads whole 256-byte rows.
+  typedef const __attribute__((address_space(1))) uint16_t* gu16;
+  uint16_t kr[kGroup], vr[kGroup];
+  int pid = 0;
+  if (has_group) {
+    if (tid < kGroup / g.P) pid = page_table[(size_t)b * pt_stride + grp * kGroup / g.P + tid];
+    const int slot0 = (grp * kGroup) % g.tail;   // ring slot of the group's first token
+#pragma unroll
+    for (int t = 0; t < kGroup; ++t) {
+      const int pos = grp * kGroup + t;
+      const bool fresh = pos >= old;
+      int slot = slot0 + t;
+      if (slot >= g.tail) slot -= g.tail;
+      const size_t row = fresh ? ((size_t)b * n_new + (pos - old)) * H + h
+                               : ((size_t)b * g.tail + slot) * H + h;
+      kr[t] = ((gu16)(fresh ? k_new : d.tail_k))[row * D + tid];
+      vr[t] = ((gu16)(fresh ? v_new : d.tail_v))[row * D + tid];
+    }
+  }
   if (FUSED && blockIdx.x == 0) {
     const int m = (int)(nw - old);
     for (int i = 0; i < m; ++i) {
@@ -111,45 +143,15 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
     }
     if (h == 0 && tid == 0) d.own_qgroups[b] = (int)q1;
   }
-  const int grp = (int)q0 + (int)blockIdx.x;
-  if (grp >= q1) return;
+  if (!has_group) return;
 
-  __shared__ float ks[kGroup][kHeadDim + 1];
-  __shared__ float vs[kGroup][kHeadDim + 1];
-  __shared__ uint8_t kcode[kGroup][kHeadDim];
-  __shared__ uint8_t vcode[kGroup][kHeadDim];
-  __shared__ uint32_t vsz[kGroup][4];
-  __shared__ int64_t page_base[kGroup / 16];
-
-  const int H = g.H, D = g.D;
-  // Stage the group's 32 tokens: positions before `old` come from the ring, later ones
-  // from this call's input. Each wave reads whole 256-byte rows; all 64 loads are issued
-  // before the first LDS store, so the staging costs one memory latency, not 32.
-  {
-    typedef const __attribute__((address_space(1))) uint16_t* gu16;
-    uint16_t kr[kGroup], vr[kGroup];
-    const int slot0 = (grp * kGroup) % g.tail;   // ring slot of the group's first token
 #pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
-      const int pos = grp * kGroup + t;
-      const bool fresh = pos >= old;
-      int slot = slot0 + t;
-      if (slot >= g.tail) slot -= g.tail;
-      const size_t row = fresh ? ((size_t)b * n_new + (pos - old)) * H + h
-                               : ((size_t)b * g.tail + slot) * H + h;
-      kr[t] = ((gu16)(fresh ? k_new : d.tail_k))[row * D + tid];
-      vr[t] = ((gu16)(fresh ? v_new : d.tail_v))[row * D + tid];
-    }
-#pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
-      ks[t][tid] = bf16_to_f32(kr[t]);
-      vs[t][tid] = bf16_to_f32(vr[t]);
-    }
+  for (int t = 0; t < kGroup; ++t) {
+    ks[t][tid] = bf16_to_f32(kr[t]);
+    vs[t][tid] = bf16_to_f32(vr[t]);
   }
   // Physical pages holding the group (one for 32-token pages, two for 16-token pages).
   if (tid < kGroup / g.P) {
-    const int lp = grp * kGroup / g.P + tid;
-    const int pid = page_table[(size_t)b * pt_stride + lp];
     if (pid < 0 || pid >= g.num_pages) {
       raise_error(g.err, kErrPage);
       page_base[tid] = -1;
