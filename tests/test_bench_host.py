@@ -1,0 +1,51 @@
+"""Host-side checks of bench.py: the multi-GPU refusal, the algorithmic byte count the roofline
+is computed from (against the oracle's byte model), and the planner-made plans."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_algorithmic_bytes_follow_the_oracle_byte_model():
+    """Per cell: every (token, head) of the history reads the source cell's bytes (the 4-bit
+    low plane weighted by the cell's hot fraction), plus q (bf16), out (fp32) and one page-table
+    entry per 32 tokens; exact tokens read 512 B."""
+    plan = np.array([[4, 2], [0, 0], [4, 2]], np.uint8)
+    B, N, H = 3, 256, 16
+    hot = np.linspace(0.1, 0.6, plan.size)
+    total, per_cell = bench.algorithmic_bytes(plan, hot, B, N, H=H)
+    i = 0
+    expect = []
+    for t in range(3):
+        for l in range(2):
+            cell = plan[t:t + 1, l:l + 1] if plan[t, l] else np.array([[plan[2, l]]], np.uint8)
+            ref = O.cache_bytes_ref(cell, num_kv_heads=H)
+            src = int(plan[2, l]) if plan[t, l] == 0 else int(plan[t, l])
+            per_tok = ref["read_hi_only"] + (hot[i] * (ref["read_all_hot"] - ref["read_hi_only"]) if src == 4 else 0)
+            expect.append(B * N * per_tok + B * H * 128 * 6 + B * (N // 32) * 4)
+            i += 1
+    assert np.allclose(per_cell, expect, rtol=1e-12)
+    assert np.isclose(total, sum(expect), rtol=1e-12)
+    # a sink and a window: 32 + 256 exact tokens at 512 B per head instead of quantized history
+    t2, _ = bench.algorithmic_bytes(plan, hot, B, N + 288, H=H, n_hist=N, n_exact=288)
+    assert np.isclose(t2 - total, len(expect) * B * 288 * H * 512 + len(expect) * B * (288 // 32) * 4, rtol=1e-12)
+
+
+def test_planner_plans_for_the_benchmark():
+    for name in ["knapsack_r", "knapsack_m"]:
+        plan = bench.knapsack_plan(name, 24, 4, 1, 32)
+        assert plan.shape == (4, 24) and set(np.unique(plan)) <= {0, 2, 4}
+        assert (plan[3] != 0).all()
