@@ -244,8 +244,10 @@ typedef struct {
  *   final loop's REUSE entry is ignored; the others must be finite.
  *   plan_out: host uint8 [num_loops * num_layers] (plan[loop * num_layers + layer]).
  *   cost_out: optional (NULL to skip).
- * Host only, no HIP call. LOOPKV_EINFEASIBLE when no plan meets the budgets (plan_out is then
- * untouched); LOOPKV_ENOTSUP beyond the size limits above. */
+ * Host only, no HIP call; it allocates about T^3 * L^4 / 4 bytes of host memory for the
+ * program's back-pointers (5 MB for 4 x 24 cells, 85 MB for 4 x 48) and frees them before it
+ * returns. LOOPKV_EINFEASIBLE when no plan meets the budgets (plan_out is then untouched);
+ * LOOPKV_ENOTSUP beyond the size limits above. */
 loopkv_status loopkv_plan_solve(const loopkv_shape* shape, const double* damage,
                                 const loopkv_plan_budget* budget, uint8_t* plan_out,
                                 loopkv_plan_cost* cost_out);
