@@ -247,7 +247,8 @@ typedef struct {
  * Host only, no HIP call; it allocates about T^3 * L^4 / 4 bytes of host memory for the
  * program's back-pointers (5 MB for 4 x 24 cells, 85 MB for 4 x 48) and frees them before it
  * returns. LOOPKV_EINFEASIBLE when no plan meets the budgets (plan_out is then untouched);
- * LOOPKV_ENOTSUP beyond the size limits above. */
+ * LOOPKV_ENOTSUP beyond the size limits above; LOOPKV_ECAPACITY if that memory is not
+ * available. */
 loopkv_status loopkv_plan_solve(const loopkv_shape* shape, const double* damage,
                                 const loopkv_plan_budget* budget, uint8_t* plan_out,
                                 loopkv_plan_cost* cost_out);

@@ -20,6 +20,7 @@
 #include <cstdint>
 #include <cstring>
 #include <limits>
+#include <new>
 #include <vector>
 
 #include "loopkv.h"
@@ -61,9 +62,11 @@ inline size_t idx(int a, int b, int c, int n) {
 
 }  // namespace
 
-extern "C" loopkv_status loopkv_plan_solve(const loopkv_shape* shape, const double* damage,
-                                           const loopkv_plan_budget* budget, uint8_t* plan_out,
-                                           loopkv_plan_cost* cost_out) {
+namespace {
+
+loopkv_status plan_solve(const loopkv_shape* shape, const double* damage,
+                         const loopkv_plan_budget* budget, uint8_t* plan_out,
+                         loopkv_plan_cost* cost_out) {
   if (!damage || !budget || !plan_out) return LOOPKV_EINVAL;
   loopkv_status st = check_shape(shape);
   if (st != LOOPKV_OK) return st;
@@ -182,4 +185,17 @@ extern "C" loopkv_status loopkv_plan_solve(const loopkv_shape* shape, const doub
     cost_out->read_bytes_per_token = b_read;
   }
   return LOOPKV_OK;
+}
+
+}  // namespace
+
+// No exception crosses the C ABI: a failed host allocation is reported as insufficient capacity.
+extern "C" loopkv_status loopkv_plan_solve(const loopkv_shape* shape, const double* damage,
+                                           const loopkv_plan_budget* budget, uint8_t* plan_out,
+                                           loopkv_plan_cost* cost_out) {
+  try {
+    return plan_solve(shape, damage, budget, plan_out, cost_out);
+  } catch (const std::bad_alloc&) {
+    return LOOPKV_ECAPACITY;
+  }
 }
