@@ -60,10 +60,6 @@ inline size_t idx(int a, int b, int c, int n) {
   return ((size_t)a * (n + 1) + b) * (n + 1) + c;
 }
 
-}  // namespace
-
-namespace {
-
 loopkv_status plan_solve(const loopkv_shape* shape, const double* damage,
                          const loopkv_plan_budget* budget, uint8_t* plan_out,
                          loopkv_plan_cost* cost_out) {
