@@ -462,7 +462,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (asked for {args.gpus}). "
-              "See DESIGN.md for how it would shard.", file=sys.stderr)
+              "Rows (request, head) are independent, so requests or heads would shard across GPUs "
+              "with no exchange.", file=sys.stderr)
         sys.exit(2)
 
     import torch

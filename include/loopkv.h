@@ -48,7 +48,7 @@ typedef enum {
   LOOPKV_OK = 0,
   LOOPKV_EINVAL = 1,    /* bad argument: null pointer, index or size out of range */
   LOOPKV_EPLAN = 2,     /* bad plan table: unknown code, or REUSE in the final loop */
-  LOOPKV_ENOTSUP = 3,   /* a shape this build does not implement */
+  LOOPKV_ENOTSUP = 3,   /* a shape this library does not implement */
   LOOPKV_ECAPACITY = 4, /* arena smaller than loopkv_cache_bytes says, or a split count
                            above shape.max_splits */
   LOOPKV_EHIP = 5,      /* a HIP runtime call or kernel launch failed */
@@ -65,7 +65,7 @@ typedef struct {
   int32_t num_loops;         /* T >= 1 */
   int32_t num_kv_heads;      /* H >= 1 */
   int32_t num_q_heads;       /* must equal num_kv_heads (no grouped-query attention) */
-  int32_t head_dim;          /* D; this build supports 128 */
+  int32_t head_dim;          /* D; this library supports 128 */
   int32_t page_tokens;       /* tokens per physical page: 16 or 32 */
   int32_t v_group;           /* value channels per scale/zero: 32, 64 or 128 */
   int32_t max_batch;         /* requests per call, at most */

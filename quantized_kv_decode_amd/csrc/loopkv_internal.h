@@ -28,7 +28,7 @@
 namespace loopkv {
 
 constexpr int kGroup = 32;     // tokens per key quantization group
-constexpr int kHeadDim = 128;  // the only head_dim this build implements
+constexpr int kHeadDim = 128;  // the only head_dim this library implements
 
 enum DeviceError : uint32_t {
   kErrLength = 1u,  // a sequence length outside [0, max context]
