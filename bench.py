@@ -16,6 +16,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -49,11 +50,22 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_hash() -> str:
+def source_digest(texts) -> str:
+    """Digest of C++ sources with comments removed and whitespace collapsed, so that only a
+    change to the code itself changes it."""
     h = hashlib.sha256()
-    for f in ["decode.hip", "loopkv_internal.h"]:
-        h.update(open(os.path.join(ROOT, "quantized_kv_decode_amd", "csrc", f), "rb").read())
+    for t in texts:
+        t = re.sub(r"/\*.*?\*/", " ", t, flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        h.update(" ".join(t.split()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_hash() -> str:
+    """Identifies the decode kernel's code: the stored HBM-traffic counters apply only while it
+    is unchanged."""
+    return source_digest(open(os.path.join(ROOT, "quantized_kv_decode_amd", "csrc", f)).read()
+                         for f in ["decode.hip", "loopkv_internal.h"])
 
 
 def build_cache(name, seed, tau, plan_name="seeded", v_group=128, shuffle=True, split_override=None):

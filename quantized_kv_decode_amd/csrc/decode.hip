@@ -12,9 +12,10 @@
 //    scale/zero fold into the attention weight and a running sum (Appendix, "History reader");
 //  - split partials merge by log-sum-exp, which gives the exact softmax (section 3.4).
 //
-// Work mapping (CDNA4, wave64): one workgroup of NW waves per (request, head, split). In each
-// round every wave takes two consecutive 32-token groups, lanes 0..31 the first and lanes
-// 32..63 the second. The group maxima are combined across the waves through LDS as a prefix
+// Work mapping (CDNA4, wave64): one workgroup per (request, RB heads, split), NW waves per
+// (request, head) row: RB = 4 rows (16 waves, one workgroup filling a CU) when the launch
+// still gives every CU a workgroup, else RB = 1. In each round every wave takes two
+// consecutive 32-token groups of its row, lanes 0..31 the first and lanes 32..63 the second. The group maxima are combined across the waves through LDS as a prefix
 // maximum, so the hot/cold decisions are exactly those of streaming the split group by group.
 // Each wave keeps its own online-softmax state; the waves merge at the end.
 //

@@ -49,3 +49,11 @@ def test_planner_plans_for_the_benchmark():
         plan = bench.knapsack_plan(name, 24, 4, 1, 32)
         assert plan.shape == (4, 24) and set(np.unique(plan)) <= {0, 2, 4}
         assert (plan[3] != 0).all()
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The stored traffic counters stay valid across comment and whitespace edits, not code edits."""
+    a = bench.source_digest(["int a; // x\n/* y\n z */ int b;\n"])
+    assert a == bench.source_digest(["int a;\n  int b; // other words\n"])
+    assert a != bench.source_digest(["int a; int c;"])
+    assert len(bench.kernel_hash()) == 16
