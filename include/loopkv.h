@@ -160,7 +160,8 @@ loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan,
 loopkv_status loopkv_plan_free(loopkv_plan plan);
 
 /* Appends new tokens to every request of cell (layer, loop).
- *   k_new_dev, v_new_dev: bf16 [batch, n_new, num_kv_heads, head_dim], contiguous.
+ *   k_new_dev, v_new_dev: bf16 [batch, n_new, num_kv_heads, head_dim], contiguous, 16-byte
+ *   aligned (LOOPKV_EINVAL otherwise).
  *   n_new_dev: optional int32 [batch]: request b appends its first n_new_dev[b] rows
  *   (0 <= n_new_dev[b] <= n_new); NULL appends all n_new rows of every request.
  *   seq_lens_dev: int32 [batch], tokens each request held before this append.
@@ -186,7 +187,8 @@ loopkv_status loopkv_quantize_append(loopkv_plan plan, int32_t layer, int32_t lo
                                      int32_t page_table_stride, void* stream);
 
 /* Decode attention of cell (layer, loop) for one query token per request.
- *   q_dev: bf16 [batch, num_q_heads, head_dim]; out_dev: fp32 [batch, num_q_heads, head_dim].
+ *   q_dev: bf16 [batch, num_q_heads, head_dim], 16-byte aligned (LOOPKV_EINVAL otherwise);
+ *   out_dev: fp32 [batch, num_q_heads, head_dim].
  *   seq_lens_dev: int32 [batch], context length including the newest token.
  * With n = seq_len, S = sink_tokens and g = max(S / 32, min(source counter, qend(n))):
  * sink = tokens [0, min(n, S)), read exactly from the cell's own sink; history = tokens

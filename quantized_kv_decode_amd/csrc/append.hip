@@ -17,7 +17,7 @@
 namespace loopkv {
 namespace {
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Round a double to the nearest fp16 (ties to even) and return its bits. One rounding,
 // straight from the double's significand.
@@ -100,56 +100,68 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
   const bool has_group = grp < q1;
 
   __shared__ float ks[kGroup][kHeadDim + 1];
-  __shared__ float vs[kGroup][kHeadDim + 1];
   __shared__ uint8_t kcode[kGroup][kHeadDim];
-  __shared__ uint8_t vcode[kGroup][kHeadDim];
-  __shared__ uint32_t vsz[kGroup][4];
   __shared__ int64_t page_base[kGroup / 16];
 
-  const int H = g.H, D = g.D;
-  // The group's page ids and its 32 tokens are requested first, so their latencies overlap
-  // each other and the ring copy below. Tokens before `old` come from the ring, later ones from
-  // this call's input; each wave reads whole 256-byte rows.
-  typedef const __attribute__((address_space(1))) uint16_t* gu16;
-  uint16_t kr[kGroup], vr[kGroup];
+  const int H = g.H, D = g.D;   // D == kHeadDim (checked on the host)
+  // Staging: thread (t, part) takes channels 32 part .. 32 part + 31 of the group's token t,
+  // four 16-byte loads each of K and V, all requested before anything waits on them (with the
+  // group's page ids). Tokens before `old` come from the ring, later ones from this call's input.
+  const int t = tid >> 2, part = tid & 3, c0 = part * 32;
+  u32x4 kw[4], vw[4];
   int pid = 0;
   if (has_group) {
     if (tid < kGroup / g.P) pid = page_table[(size_t)b * pt_stride + grp * kGroup / g.P + tid];
-    const int slot0 = (grp * kGroup) % g.tail;   // ring slot of the group's first token
+    const int pos = grp * kGroup + t;
+    const bool fresh = pos >= old;
+    int slot = (grp * kGroup) % g.tail + t;   // ring slot of the token
+    if (slot >= g.tail) slot -= g.tail;
+    const size_t row = fresh ? ((size_t)b * n_new + (pos - old)) * H + h
+                             : ((size_t)b * g.tail + slot) * H + h;
+    const u32x4* kp = reinterpret_cast<const u32x4*>((fresh ? k_new : d.tail_k) + row * D + c0);
+    const u32x4* vp = reinterpret_cast<const u32x4*>((fresh ? v_new : d.tail_v) + row * D + c0);
 #pragma unroll
-    for (int t = 0; t < kGroup; ++t) {
-      const int pos = grp * kGroup + t;
-      const bool fresh = pos >= old;
-      int slot = slot0 + t;
-      if (slot >= g.tail) slot -= g.tail;
-      const size_t row = fresh ? ((size_t)b * n_new + (pos - old)) * H + h
-                               : ((size_t)b * g.tail + slot) * H + h;
-      kr[t] = ((gu16)(fresh ? k_new : d.tail_k))[row * D + tid];
-      vr[t] = ((gu16)(fresh ? v_new : d.tail_v))[row * D + tid];
+    for (int i = 0; i < 4; ++i) {
+      kw[i] = kp[i];
+      vw[i] = vp[i];
     }
   }
   if (FUSED && blockIdx.x == 0) {
+    // The call's tokens of this head into the ring (and the sink): 16 bytes per thread.
     const int m = (int)(nw - old);
-    for (int i = 0; i < m; ++i) {
-      const size_t src = (((size_t)b * n_new + i) * g.H + h) * g.D + tid;
-      const size_t dst = (((size_t)b * g.tail + (old + i) % g.tail) * g.H + h) * g.D + tid;
-      d.tail_k[dst] = k_new[src];
-      d.tail_v[dst] = v_new[src];
+    for (int e = tid; e < m * (kHeadDim / 8); e += 128) {
+      const int i = e / (kHeadDim / 8), ch = (e % (kHeadDim / 8)) * 8;
+      const size_t src = (((size_t)b * n_new + i) * g.H + h) * g.D + ch;
+      const size_t dst = (((size_t)b * g.tail + (old + i) % g.tail) * g.H + h) * g.D + ch;
+      const u32x4 kx = *reinterpret_cast<const u32x4*>(k_new + src);
+      const u32x4 vx = *reinterpret_cast<const u32x4*>(v_new + src);
+      *reinterpret_cast<u32x4*>(d.tail_k + dst) = kx;
+      *reinterpret_cast<u32x4*>(d.tail_v + dst) = vx;
       if (old + i < g.sink) {
-        const size_t sd = (((size_t)b * g.sink + old + i) * g.H + h) * g.D + tid;
-        d.sink_k[sd] = k_new[src];
-        d.sink_v[sd] = v_new[src];
+        const size_t sd = (((size_t)b * g.sink + old + i) * g.H + h) * g.D + ch;
+        *reinterpret_cast<u32x4*>(d.sink_k + sd) = kx;
+        *reinterpret_cast<u32x4*>(d.sink_v + sd) = vx;
       }
     }
     if (h == 0 && tid == 0) d.own_qgroups[b] = (int)q1;
   }
   if (!has_group) return;
 
+  float kv[32], vv[32];
 #pragma unroll
-  for (int t = 0; t < kGroup; ++t) {
-    ks[t][tid] = bf16_to_f32(kr[t]);
-    vs[t][tid] = bf16_to_f32(vr[t]);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t kx[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+    const uint32_t vx[4] = {vw[i].x, vw[i].y, vw[i].z, vw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kv[8 * i + 2 * j] = __uint_as_float(kx[j] << 16);
+      kv[8 * i + 2 * j + 1] = __uint_as_float(kx[j] & 0xFFFF0000u);
+      vv[8 * i + 2 * j] = __uint_as_float(vx[j] << 16);
+      vv[8 * i + 2 * j + 1] = __uint_as_float(vx[j] & 0xFFFF0000u);
+    }
   }
+#pragma unroll
+  for (int c = 0; c < 32; ++c) ks[t][c0 + c] = kv[c];
   // Physical pages holding the group (one for 32-token pages, two for 16-token pages).
   if (tid < kGroup / g.P) {
     if (pid < 0 || pid >= g.num_pages) {
@@ -165,86 +177,85 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
 
   const Layout lay = head_layout(BITS, g.P, D, g.nvg);
   const int64_t hoff = (int64_t)h * lay.total;
+  // The head block of the page holding token tt of the group, and tt's row in that page.
+  auto tok_block = [&](int tt, int* tl) -> uint8_t* {
+    *tl = tt % g.P;
+    return d.own_pool + page_base[tt / g.P] + hoff;
+  };
+
+  // Values: the thread's 32 channels of token t; a group wider than 32 channels combines its
+  // min/max across the neighbouring lanes that hold its other channels.
+  {
+    float mnf = vv[0], mxf = vv[0];
+#pragma unroll
+    for (int c = 1; c < 32; ++c) {
+      mnf = vv[c] < mnf ? vv[c] : mnf;
+      mxf = vv[c] > mxf ? vv[c] : mxf;
+    }
+    for (int w = 1; w < g.v_group / 32; w <<= 1) {
+      const float omn = __shfl_xor(mnf, w), omx = __shfl_xor(mxf, w);
+      mnf = omn < mnf ? omn : mnf;
+      mxf = omx > mxf ? omx : mxf;
+    }
+    const double mn = mnf, mx = mxf;
+    const uint16_t sb = f64_to_f16_bits((mx - mn) / (double)L);
+    const uint16_t zb = f64_to_f16_bits(mn);
+    const double s = f16_bits_to_f64(sb), z = f16_bits_to_f64(zb);
+    int tl;
+    uint8_t* blk = tok_block(t, &tl);
+    // two 16-channel words (channel 16 cb + i at bits 2i): the high plane / INT2 codes, and for
+    // INT4 the low plane
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t hiw = 0, low = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t c = (uint32_t)quant_code(vv[16 * half + i], s, z, L);
+        if (BITS == 4) {
+          hiw |= (c >> 2) << (2 * i);
+          low |= (c & 3u) << (2 * i);
+        } else {
+          hiw |= c << (2 * i);
+        }
+      }
+      const int cb = 2 * part + half;
+      reinterpret_cast<uint32_t*>(blk + lay.vc)[cb * g.P + tl] = hiw;
+      if (BITS == 4) reinterpret_cast<uint32_t*>(blk + lay.vlo)[tl * (kHeadDim / 16) + cb] = low;
+    }
+    if (c0 % g.v_group == 0)
+      reinterpret_cast<uint32_t*>(blk + lay.vsz)[tl * g.nvg + c0 / g.v_group] =
+          (uint32_t)sb | ((uint32_t)zb << 16);
+  }
 
   // Keys: thread = channel; min/max over the group's tokens.
   {
     const int c = tid;
-    double mn = ks[0][c], mx = mn;
-    for (int t = 1; t < kGroup; ++t) {
-      const double x = ks[t][c];
-      mn = x < mn ? x : mn;
-      mx = x > mx ? x : mx;
+    float mnf = ks[0][c], mxf = mnf;
+    for (int tt = 1; tt < kGroup; ++tt) {
+      const float x = ks[tt][c];
+      mnf = x < mnf ? x : mnf;
+      mxf = x > mxf ? x : mxf;
     }
+    const double mn = mnf, mx = mxf;
     const uint16_t sb = f64_to_f16_bits((mx - mn) / (double)L);
     const uint16_t zb = f64_to_f16_bits(mn);
     const double s = f16_bits_to_f64(sb), z = f16_bits_to_f64(zb);
-    for (int t = 0; t < kGroup; ++t) kcode[t][c] = (uint8_t)quant_code(ks[t][c], s, z, L);
+    for (int tt = 0; tt < kGroup; ++tt) kcode[tt][c] = (uint8_t)quant_code(ks[tt][c], s, z, L);
     uint8_t* blk = d.own_pool + page_base[0] + hoff;
     reinterpret_cast<uint32_t*>(blk + lay.ksz)[c] = (uint32_t)sb | ((uint32_t)zb << 16);
   }
-  // Values: four threads per token, 32 channels each; groups wider than 32 channels
-  // combine their min/max across neighbouring lanes.
-  {
-    const int t = tid >> 2, part = tid & 3, c0 = part * 32;
-    double mn = vs[t][c0], mx = mn;
-    for (int c = 1; c < 32; ++c) {
-      const double x = vs[t][c0 + c];
-      mn = x < mn ? x : mn;
-      mx = x > mx ? x : mx;
-    }
-    for (int w = 1; w < g.v_group / 32; w <<= 1) {
-      const double omn = __shfl_xor(mn, w), omx = __shfl_xor(mx, w);
-      mn = omn < mn ? omn : mn;
-      mx = omx > mx ? omx : mx;
-    }
-    const uint16_t sb = f64_to_f16_bits((mx - mn) / (double)L);
-    const uint16_t zb = f64_to_f16_bits(mn);
-    const double s = f16_bits_to_f64(sb), z = f16_bits_to_f64(zb);
-    for (int c = 0; c < 32; ++c) vcode[t][c0 + c] = (uint8_t)quant_code(vs[t][c0 + c], s, z, L);
-    if (c0 % g.v_group == 0) vsz[t][c0 / g.v_group] = (uint32_t)sb | ((uint32_t)zb << 16);
-  }
   __syncthreads();
 
-  // Pack words and store them into the page(s).
-  auto tok_block = [&](int t, int* tl) -> uint8_t* {
-    const int pos_in_grp = t;
-    const int pi = pos_in_grp / g.P;
-    *tl = pos_in_grp % g.P;
-    return d.own_pool + page_base[pi] + hoff;
-  };
-  constexpr int KPW = 32 / BITS;  // key channels per word
+  // Key code words W[cb][t]: KPW channels of one token per word.
+  constexpr int KPW = 32 / BITS;
   for (int w = tid; w < (kHeadDim / KPW) * kGroup; w += 128) {
-    const int cb = w / kGroup, t = w % kGroup;
+    const int cb = w / kGroup, tt = w % kGroup;
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) word |= (uint32_t)kcode[t][cb * KPW + i] << (BITS * i);
+    for (int i = 0; i < KPW; ++i) word |= (uint32_t)kcode[tt][cb * KPW + i] << (BITS * i);
     int tl;
-    uint8_t* blk = tok_block(t, &tl);
+    uint8_t* blk = tok_block(tt, &tl);
     reinterpret_cast<uint32_t*>(blk + lay.kc)[cb * g.P + tl] = word;
-  }
-  for (int w = tid; w < (kHeadDim / 16) * kGroup; w += 128) {
-    const int cb = w / kGroup, t = w % kGroup;
-    uint32_t hiw = 0, low = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t c = vcode[t][cb * 16 + i];
-      if (BITS == 4) {
-        hiw |= (c >> 2) << (2 * i);
-        low |= (c & 3u) << (2 * i);
-      } else {
-        hiw |= c << (2 * i);
-      }
-    }
-    int tl;
-    uint8_t* blk = tok_block(t, &tl);
-    reinterpret_cast<uint32_t*>(blk + lay.vc)[cb * g.P + tl] = hiw;
-    if (BITS == 4) reinterpret_cast<uint32_t*>(blk + lay.vlo)[tl * (kHeadDim / 16) + cb] = low;
-  }
-  for (int w = tid; w < kGroup * g.nvg; w += 128) {
-    const int t = w / g.nvg, vg = w % g.nvg;
-    int tl;
-    uint8_t* blk = tok_block(t, &tl);
-    reinterpret_cast<uint32_t*>(blk + lay.vsz)[tl * g.nvg + vg] = vsz[t][vg];
   }
 }
 

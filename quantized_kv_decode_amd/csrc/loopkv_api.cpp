@@ -324,6 +324,7 @@ loopkv_status loopkv_quantize_append(loopkv_plan p, int32_t layer, int32_t loop,
                                      int32_t pt_stride, void* stream) {
   if (!cell_ok(p, layer, loop)) return LOOPKV_EINVAL;
   if (!k_new || !v_new || !seq_lens || !page_table) return LOOPKV_EINVAL;
+  if (((uintptr_t)k_new | (uintptr_t)v_new) % 16 != 0) return LOOPKV_EINVAL;   // 16-byte rows
   if (batch < 1 || batch > p->shape.max_batch || n_new < 0 || pt_stride < 1) return LOOPKV_EINVAL;
   if ((int64_t)n_new > (int64_t)p->shape.max_pages_per_seq * p->shape.page_tokens)
     return LOOPKV_EINVAL;
@@ -343,6 +344,7 @@ loopkv_status loopkv_decode_attention(loopkv_plan p, int32_t layer, int32_t loop
                                       void* stream) {
   if (!cell_ok(p, layer, loop)) return LOOPKV_EINVAL;
   if (!q || !seq_lens || !page_table || !out) return LOOPKV_EINVAL;
+  if ((uintptr_t)q % 16 != 0) return LOOPKV_EINVAL;   // read in 16-byte pieces
   if (batch < 1 || batch > p->shape.max_batch || pt_stride < 1) return LOOPKV_EINVAL;
   loopkv_decode_opts o;
   std::memset(&o, 0, sizeof(o));

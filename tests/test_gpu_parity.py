@@ -83,6 +83,14 @@ def test_decode_one_layer_four_loops(variant):
     plan = np.array([[4], [4], [2 if variant == "A" else 0], [4]], np.uint8)
     log(f"decode 1x4 plan {variant}")
     w = Workload(plan, batch=8, lens=[4096] * 8, seed=21)
+    if variant == "B":
+        # the reusing cell's descriptor reads the final loop's pool and stores nothing
+        # (section 3.2, C2)
+        reuse, src = w.cache.cell_info(0, 2), w.cache.cell_info(0, 3)
+        assert reuse.code == 0 and reuse.own_pool_dev is None
+        assert reuse.read_pool_dev == src.own_pool_dev == src.read_pool_dev
+        assert (reuse.read_bits, reuse.gated, reuse.page_bytes) == (4, 1, src.page_bytes)
+        assert reuse.qgroups_dev is None or reuse.qgroups_dev != src.qgroups_dev
     w.append_upto(w.lens)
     seq = torch.full((8,), 4096, dtype=torch.int32, device="cuda")
     for t in range(4):
@@ -133,6 +141,32 @@ def test_decode_empty_and_tail_only_rows():
     ref, _ = w.oracle_decode(0, 0, q, tau=0.01)
     assert torch.all(out[0] == 0)
     check_out(out, ref, "short rows")
+
+
+def test_misaligned_inputs_rejected_before_launch():
+    """k_new, v_new and q are read in 16-byte pieces: a pointer off that alignment is an
+    argument error, and nothing is enqueued."""
+    w = Workload([[4]], batch=2, lens=[40, 40], seed=52)
+    w.append_upto([32, 32])
+    before = w.cache.own_pool(0, 0).clone()
+    kk = torch.zeros(2 * 8 * 16 * 128 + 8, dtype=torch.bfloat16, device="cuda")
+    k_off = kk[1:1 + 2 * 8 * 16 * 128]                      # 2 bytes past an aligned base
+    seq = w.seq_lens(0, 0)
+    for args in [(k_off.data_ptr(), kk.data_ptr()), (kk.data_ptr(), k_off.data_ptr())]:
+        with pytest.raises(L.LoopKVError) as e:
+            L.loopkv_quantize_append(w.cache.handle, 0, 0, *args, 2, 8, None, seq.data_ptr(),
+                                     w.page_table.data_ptr(), w.page_table.stride(0), 0)
+        assert e.value.status == L.EINVAL
+    q = torch.zeros(2 * 16 * 128 + 8, dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros(2, 16, 128, dtype=torch.float32, device="cuda")
+    with pytest.raises(L.LoopKVError) as e:
+        L.loopkv_decode_attention(w.cache.handle, 0, 0, q[1:].data_ptr(), 2, seq.data_ptr(),
+                                  w.page_table.data_ptr(), w.page_table.stride(0), None,
+                                  out.data_ptr(), 0)
+    assert e.value.status == L.EINVAL
+    torch.cuda.synchronize()
+    assert torch.equal(w.cache.own_pool(0, 0), before) and torch.all(out == 0)
+    assert w.cache.device_errors() == 0
 
 
 def test_device_errors_flag_bad_lengths():
