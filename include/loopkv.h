@@ -49,8 +49,8 @@ typedef enum {
   LOOPKV_EINVAL = 1,    /* bad argument: null pointer, index or size out of range */
   LOOPKV_EPLAN = 2,     /* bad plan table: unknown code, or REUSE in the final loop */
   LOOPKV_ENOTSUP = 3,   /* a shape this library does not implement */
-  LOOPKV_ECAPACITY = 4, /* arena smaller than loopkv_cache_bytes says, or a split count
-                           above shape.max_splits */
+  LOOPKV_ECAPACITY = 4, /* arena smaller than loopkv_cache_bytes says, a split count
+                           above shape.max_splits, or host memory exhausted */
   LOOPKV_EHIP = 5,      /* a HIP runtime call or kernel launch failed */
   LOOPKV_EINFEASIBLE = 6 /* loopkv_plan_solve: no plan meets the budgets */
 } loopkv_status;

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <memory>
 #include <new>
 #include <vector>
 
@@ -198,8 +199,10 @@ const char* loopkv_status_string(loopkv_status st) {
   return "unknown status";
 }
 
+// Host allocations that fail inside an entry point are reported as insufficient capacity; no
+// exception crosses the C ABI.
 loopkv_status loopkv_cache_bytes(const loopkv_shape* shape, const uint8_t* plan,
-                                 loopkv_bytes* out) {
+                                 loopkv_bytes* out) try {
   if (!out) return LOOPKV_EINVAL;
   loopkv_status st = check_shape(shape);
   if (st != LOOPKV_OK) return st;
@@ -210,10 +213,12 @@ loopkv_status loopkv_cache_bytes(const loopkv_shape* shape, const uint8_t* plan,
   if (st != LOOPKV_OK) return st;
   *out = a.bytes;
   return LOOPKV_OK;
+} catch (const std::bad_alloc&) {
+  return LOOPKV_ECAPACITY;
 }
 
 loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan, void* arena_dev,
-                               uint64_t arena_bytes, void* stream, loopkv_plan* out) {
+                               uint64_t arena_bytes, void* stream, loopkv_plan* out) try {
   if (!out) return LOOPKV_EINVAL;
   *out = nullptr;
   loopkv_status st = check_shape(shape);
@@ -226,8 +231,7 @@ loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan, v
   if (st != LOOPKV_OK) return st;
   if (arena_bytes < a.total) return LOOPKV_ECAPACITY;
 
-  loopkv_plan_s* p = new (std::nothrow) loopkv_plan_s;
-  if (!p) return LOOPKV_EINVAL;
+  std::unique_ptr<loopkv_plan_s> p(new loopkv_plan_s);
   p->shape = *shape;
   const int T = shape->num_loops, L = shape->num_layers, H = shape->num_kv_heads;
   const int nvg = shape->head_dim / shape->v_group;
@@ -273,12 +277,11 @@ loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan, v
     e = hipMemsetAsync(counters, 0, (size_t)T * L * shape->max_batch * sizeof(int32_t), s);
   if (e == hipSuccess) e = hipMemsetAsync(p->err_dev, 0, sizeof(uint32_t), s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
-  if (e != hipSuccess) {
-    delete p;
-    return LOOPKV_EHIP;
-  }
-  *out = p;
+  if (e != hipSuccess) return LOOPKV_EHIP;
+  *out = p.release();
   return LOOPKV_OK;
+} catch (const std::bad_alloc&) {
+  return LOOPKV_ECAPACITY;
 }
 
 loopkv_status loopkv_plan_free(loopkv_plan plan) {
