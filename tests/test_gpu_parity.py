@@ -198,3 +198,24 @@ def test_decode_value_groups(v_group):
             check_out(out, ref, f"G={v_group} loop {t} tau {tau} split {split}")
             w.check_masks(mask, hot, t, 0, q, tau, split)
     assert w.cache.device_errors() == 0
+
+
+@pytest.mark.parametrize("heads,batch", [(1, 3), (6, 3), (20, 52)])
+def test_decode_head_counts(heads, batch):
+    """Head counts off the 16-head shape: 1 and 6 heads (one head per workgroup) and 20 heads x
+    52 requests (260 four-head workgroups on 256 CUs: more than one generation, so requests are
+    taken longest first). Plan [4, 2, REUSE, 4], ragged lengths, tau 0.02."""
+    plan = np.array([[4], [2], [0], [4]], np.uint8)
+    rng = np.random.default_rng(300 + heads)
+    lens = rng.integers(33, 230, size=batch).astype(np.int32)
+    log(f"decode heads={heads} batch={batch}")
+    w = Workload(plan, batch=batch, lens=lens, heads=heads, seed=91 + heads)
+    w.append_upto(w.lens, chunk=100)
+    for t in range(4):
+        q = synth.queries(batch, heads, 128, 700 + 10 * heads + t)
+        mask = _mask_buf(w)
+        out = w.cache.decode(0, t, q.cuda(), w.seq_lens(t, 0), w.page_table, tau=0.02, fetch_mask=mask)
+        ref, hot = w.oracle_decode(t, 0, q, tau=0.02)
+        check_out(out, ref, f"heads {heads} loop {t}")
+        w.check_masks(mask, hot, t, 0, q, 0.02, 0)
+    assert w.cache.device_errors() == 0
