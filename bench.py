@@ -267,8 +267,23 @@ def cpu_baseline(cfg, plan, tau, seed, budget_s=12.0):
     us_step = timed / done * rows_step * 1e6
     return {"value": round(us_step, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
             "sample": f"{done} (request, head) decodes of {N} tokens from {len(rows)} packed rows of "
-                      f"{len(cells)} cells (INT4 / INT2 / reuse), {timed:.1f} s on one core; "
-                      f"extrapolated x{rows_step / done:.0f} to the {rows_step} rows of one step"}
+                      f"{len(cells)} cells (INT4 / INT2 / reuse), {timed:.1f} s on one core of "
+                      f"{host_cpu()}; extrapolated x{rows_step / done:.0f} to the {rows_step} rows "
+                      f"of one step"}
+
+
+def host_cpu() -> str:
+    """The host's CPU model and how many cores this process may run on."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{len(os.sched_getaffinity(0))} available ({model})"
 
 
 def run_paged(args):
