@@ -61,6 +61,23 @@ __device__ __forceinline__ int quant_code(double x, double s, double z, int leve
   return (int)c;
 }
 
+// The same code from an fp32 estimate. With x exact (bf16), s and z exact (fp16) and
+// u = (x - z) * rcp(s) + 1/2 formed in fp32, |u - ((x - z) / s + 1/2)| < 6e-6 whenever the
+// result can land inside [0, levels] (a relative error below 2^-22 on values up to 17). So
+// when u is at least kBand = 1e-5 away from an integer, floor(u) is the floor of the exact
+// value, which the fp64 rule also reaches (its own error is ~1e-15); nearer a boundary, or for
+// values that are not finite, the fp64 rule decides. The estimate saves the fp64 division.
+__device__ __forceinline__ int quant_code_fast(float x, float s32, float z32, double s, double z,
+                                               int levels) {
+  constexpr float kBand = 1e-5f;
+  if (s32 == 0.f) return 0;
+  const float u = fmaf(x - z32, __builtin_amdgcn_rcpf(s32), 0.5f);
+  const float f = floorf(u);
+  const float d = fminf(u - f, f + 1.f - u);   // distance to the nearest integer
+  if (!(d >= kBand) || !(u < 4096.f)) return quant_code((double)x, s, z, levels);
+  return (int)fminf(fmaxf(f, 0.f), (float)levels);
+}
+
 __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t flag) { atomicOr(err, flag); }
 
 // One workgroup of 128 threads quantizes one 32-token key group that leaves the window, of one
@@ -201,6 +218,7 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
     const uint16_t sb = f64_to_f16_bits((mx - mn) / (double)L);
     const uint16_t zb = f64_to_f16_bits(mn);
     const double s = f16_bits_to_f64(sb), z = f16_bits_to_f64(zb);
+    const float s32 = (float)s, z32 = (float)z;   // exact: fp16 values
     int tl;
     uint8_t* blk = tok_block(t, &tl);
     // two 16-channel words (channel 16 cb + i at bits 2i): the high plane / INT2 codes, and for
@@ -210,7 +228,7 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
       uint32_t hiw = 0, low = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t c = (uint32_t)quant_code(vv[16 * half + i], s, z, L);
+        const uint32_t c = (uint32_t)quant_code_fast(vv[16 * half + i], s32, z32, s, z, L);
         if (BITS == 4) {
           hiw |= (c >> 2) << (2 * i);
           low |= (c & 3u) << (2 * i);
@@ -240,7 +258,9 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
     const uint16_t sb = f64_to_f16_bits((mx - mn) / (double)L);
     const uint16_t zb = f64_to_f16_bits(mn);
     const double s = f16_bits_to_f64(sb), z = f16_bits_to_f64(zb);
-    for (int tt = 0; tt < kGroup; ++tt) kcode[tt][c] = (uint8_t)quant_code(ks[tt][c], s, z, L);
+    const float s32 = (float)s, z32 = (float)z;   // exact: fp16 values
+    for (int tt = 0; tt < kGroup; ++tt)
+      kcode[tt][c] = (uint8_t)quant_code_fast(ks[tt][c], s32, z32, s, z, L);
     uint8_t* blk = d.own_pool + page_base[0] + hoff;
     reinterpret_cast<uint32_t*>(blk + lay.ksz)[c] = (uint32_t)sb | ((uint32_t)zb << 16);
   }
