@@ -219,3 +219,34 @@ def test_decode_head_counts(heads, batch):
         check_out(out, ref, f"heads {heads} loop {t}")
         w.check_masks(mask, hot, t, 0, q, 0.02, 0)
     assert w.cache.device_errors() == 0
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_append_half_step_ties(bits):
+    """Values exactly half a step above a code, x = z + (k + 1/2) s, for scales 1, 3, 5, 7 and 3/8
+    and zero points 0, -7 and 2 (all exact in bf16 / fp16): the rounding rule rounds them up.
+    The kernel's fp32 estimate sits on the boundary there (and with an inexact reciprocal of s
+    may fall on either side), so the fp64 rule must decide. Keys along channels' groups, values
+    along tokens' channels; pool bytes must equal the oracle's."""
+    levels = (1 << bits) - 1
+    w = Workload([[bits]], batch=1, lens=[64], seed=57)
+    cases = [(1.0, 0.0), (3.0, 0.0), (5.0, -7.0), (7.0, 2.0), (0.375, -7.0), (3.0, 2.0)]
+
+    def pattern(step, zero, n):
+        ties = [zero, zero + levels * step] + [zero + (k + 0.5) * step for k in range(levels)]
+        return torch.tensor((ties * n)[:n], dtype=torch.float64).to(torch.bfloat16), ties
+
+    for j, (step, zero) in enumerate(cases):
+        col, ties = pattern(step, zero, 32)
+        assert torch.equal(col.double(), torch.tensor((ties * 32)[:32], dtype=torch.float64))
+        w.k[0, 0][0, :32, 1 + j % 3, 7 + 11 * j] = col
+        row, _ = pattern(step, zero, 128)
+        w.v[0, 0][0, 33 + 2 * j, 2, :] = row
+    w.append_upto(w.lens)
+    qh = w.quant(0, 0)
+    for j, (step, zero) in enumerate(cases):
+        kc = qh[0][1 + j % 3].k_codes[:32, 7 + 11 * j]
+        assert list(kc[2:2 + levels]) == list(range(1, levels + 1)), (step, zero)
+    pool = w.cache.own_pool(0, 0).cpu().numpy()
+    ref = O.pack_pool(bits, 32, qh, w.page_table_np, w.num_pages, 128)
+    assert np.array_equal(pool, ref)
