@@ -15,15 +15,16 @@
 // Work mapping (CDNA4, wave64): one workgroup per (request, RB heads, split), NW waves per
 // (request, head) row: RB = 4 rows (16 waves, one workgroup filling a CU) when the launch
 // still gives every CU a workgroup, else RB = 1. In each round every wave takes two
-// consecutive 32-token groups of its row, lanes 0..31 the first and lanes 32..63 the second. The group maxima are combined across the waves through LDS as a prefix
-// maximum, so the hot/cold decisions are exactly those of streaming the split group by group.
+// consecutive 32-token groups of its row, lanes 0..31 the first and lanes 32..63 the second.
+// The group maxima are combined across the waves through LDS as a prefix maximum, so the
+// hot/cold decisions are exactly those of streaming the split group by group.
 // Each wave keeps its own online-softmax state; the waves merge at the end.
 //
 // Latency hiding: each part of a wave's next two groups (key codes and scales, value scales,
 // value high plane or INT2 codes) is loaded right after this round's last use of the same
 // registers, so it has about a round to arrive; page ids are read a round before the loads
 // that use them; the low planes of a round's hot tokens are loaded in that round and added in
-// the next.
+// the next, before that round's barrier, where a wave would otherwise wait for the others.
 //
 // Arithmetic:
 //  - keys: a 4-bit code in the low bits of an fp8 (E4M3) byte converts exactly to code * u
@@ -469,6 +470,9 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
       sm.gmax[rd & 1][w][0] = gmA;
       sm.gmax[rd & 1][w][1] = gmB;
     }
+    // Last round's low planes, before this round can move the wave's maximum; done before the
+    // barrier, while the other waves are still forming their scores.
+    add_prev_lo<NVG, NW>(sm, st, (rd + 1) & 1, w, lane, k.mk);
     __syncthreads();
     // Group maxima of this round in stream order: wave i's groups are 2i and 2i+1.
     const float* gx = &sm.gmax[rd & 1][0][0];
@@ -482,9 +486,6 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
     mpreB = dmax(mpreA, gmB);
     st.m_run = mall;
   }
-
-  // ---- last round's low planes, before this round can move the wave's maximum
-  if (BITS == 4) add_prev_lo<NVG, NW>(sm, st, (rd + 1) & 1, w, lane, k.mk);
 
   // ---- online softmax: rescale only when the wave's maximum grows
   const float gm = dmax(gmA, gmB);
