@@ -10,7 +10,7 @@ Shapes: the 96-cell 8K batch-64 cache (32-token pages), the paged serving batch 
 1K..16K tokens, 16-token pages in a shuffled table, one appended token per request per cell
 before the decode), and the long-context shape (batch 16, 32K tokens, heavy-tailed keys,
 8K-token splits merged by log-sum-exp), and the 8K batch-64 shape again with a 32-token sink and a
-256-token window kept exact."""
+256-token window kept exact, and with 32-channel value groups (the paper's KIVI groups)."""
 import math
 
 import numpy as np
@@ -28,7 +28,7 @@ pytestmark = pytest.mark.gpu
 PLAN = np.array([[4], [2], [0], [4]], np.uint8)   # loop 3 reuses the final loop's KV
 
 
-def _run_case(name, *, B, lens, P, split, heavy, seed, rows_per_cell, append_one, S=0, W=0):
+def _run_case(name, *, B, lens, P, split, heavy, seed, rows_per_cell, append_one, S=0, W=0, VG=128):
     H, D, tau = 16, 128, 0.01
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens, np.int64)
@@ -36,7 +36,7 @@ def _run_case(name, *, B, lens, P, split, heavy, seed, rows_per_cell, append_one
     pt_np, npages = synth.page_table(lens, P, seed + 1, shuffle=True)
     pt = torch.as_tensor(pt_np).cuda()
     max_splits = max(1, int(pt_np.shape[1] * P // split)) if split else 1
-    shape = L.make_shape(num_layers=1, num_loops=4, num_kv_heads=H, page_tokens=P, v_group=128,
+    shape = L.make_shape(num_layers=1, num_loops=4, num_kv_heads=H, page_tokens=P, v_group=VG,
                          max_batch=B, max_pages_per_seq=pt_np.shape[1],
                          tail_tokens=64 if W == 0 else W + 64, max_splits=max_splits,
                          num_pages=npages, sink_tokens=S, window_tokens=W)
@@ -109,7 +109,7 @@ def _run_case(name, *, B, lens, P, split, heavy, seed, rows_per_cell, append_one
             # sink [0, se), quantized history [S, he), exact tail [he, n)
             se, _, he = O.near_far_split(n, S, W)
             ks, vs = kv_rows[src, b, h]
-            qh = O.quantize_head(ks[S:he], vs[S:he], bits, 128)
+            qh = O.quantize_head(ks[S:he], vs[S:he], bits, VG)
             kt, vt = kv_rows[t, b, h]
             ref, hot, s = O.decode_head(q64[b, h], qh, kt[he:n], vt[he:n], sm_scale=1 / math.sqrt(D),
                                         tau=tau, split_tokens=split, sink_k=kt[:se], sink_v=vt[:se],
@@ -150,3 +150,10 @@ def test_fullsize_ouro14b_b64_ctx8k_sink_window():
     256-token window stay exact, the 7904 tokens between are quantized history."""
     _run_case("b64-ctx8k-sink-window", B=64, lens=[8192] * 64, P=32, split=0, heavy=False, seed=304,
               rows_per_cell=8, append_one=False, S=32, W=256)
+
+
+def test_fullsize_ouro14b_b64_ctx8k_value_groups_32():
+    """The benchmark's per-cell shape with 32-channel value groups (four value scales per token
+    and head), as in the paper's KIVI configurations."""
+    _run_case("b64-ctx8k-vg32", B=64, lens=[8192] * 64, P=32, split=0, heavy=False, seed=305,
+              rows_per_cell=8, append_one=False, VG=32)
