@@ -57,3 +57,26 @@ def test_kernel_hash_ignores_comments_only():
     assert a == bench.source_digest(["int a;\n  int b; // other words\n"])
     assert a != bench.source_digest(["int a; int c;"])
     assert len(bench.kernel_hash()) == 16
+
+
+def test_cpu_baseline_all_cores_child(tmp_path):
+    """The all-cores CPU baseline: the sample written to disk is read back by a child Python
+    (importing no GPU library), which runs one oracle worker per available core and reports how
+    many rows each decoded in how long."""
+    from quantized_kv_decode_amd import synth
+    B, N, H = 2, 64, 16
+    k = synth.keys(B, N, H, 128, 5)[0].double().numpy()
+    v = synth.values(B, N, H, 128, 5)[0].double().numpy()
+    q = synth.queries(B, H, 128, 6).double().numpy()
+    heads = [O.quantize_head(k[:, h], v[:, h], 4, 128) for h in range(H)]
+    pool = O.pack_pool(4, 32, [heads], np.arange(N // 32)[None, :], N // 32)
+    cells = [(4, pool)]
+    rows = [(0, h, q[:, h].copy(), k[:0, h], v[:0, h], k[N:, h], v[N:, h]) for h in range(3)]
+    cfg = dict(B=B, N=N, S=0, n_hist=N, split=0)
+    t, d = bench._time_rows(cells, rows, cfg, 0.01, 0.05)
+    assert d >= 1 and t > 0
+    path = str(tmp_path / "sample.npz")
+    bench._write_sample(path, cells, rows, cfg, 0.01, 0.2)
+    pj = bench._run_pool(path, 0.2)
+    assert pj["workers"] >= 1 and len(pj["runs"]) == pj["workers"]
+    assert all(dd >= 1 and tt > 0 for tt, dd in pj["runs"])
