@@ -104,3 +104,26 @@ def test_invalid_and_infeasible():
     with pytest.raises(L.LoopKVError) as e:
         L.loopkv_plan_solve(_shape(2, 6), synth.damage_table(2, 6, 1))
     assert e.value.status == L.ENOTSUP
+
+
+@pytest.mark.parametrize("T,Lr", [(1, 3), (5, 1)])
+def test_loop_count_limits_match_enumeration(T, Lr):
+    """One loop (every cell is the final loop: no reuse option) and five loops (the largest
+    supported: 2 * 3^4 whole-layer choices), against the oracle's enumeration of every plan."""
+    rng = np.random.default_rng(500 + T)
+    d = rng.lognormal(-3, 1.0, size=(T, Lr, 3))
+    d[:, :, 1] += d[:, :, 0]
+    d[T - 1, :, 2] = np.nan
+    d4 = float(d[:, :, 0].sum())
+    all4 = O.plan_cost(np.full((T, Lr), 4, np.uint8), d)[1]
+    for md, ms in [(-1.0, 0.0), (d4 * 2.0, 0.0), (d4 * 3.0, all4 * 0.7)]:
+        pe, ce = O.plan_exhaustive(d, md, ms)
+        if pe is None:
+            with pytest.raises(L.LoopKVError):
+                L.loopkv_plan_solve(_shape(Lr, T), d, md, ms)
+            continue
+        plan, cost = L.loopkv_plan_solve(_shape(Lr, T), d, md, ms)
+        c = _check_valid(plan, cost, d, md, ms)
+        assert abs(c[2] - ce[2]) <= 1e-6 and abs(c[0] - ce[0]) <= 1e-12 * max(1.0, ce[0])
+        if T == 1:
+            assert (plan != 0).all()
