@@ -3,6 +3,8 @@
 Codes, planes, scales and rings must match byte for byte; fetch masks bit for bit except
 tokens whose test value lies within 1e-6 of tau; outputs within 2e-3 of the oracle's largest
 magnitude per call."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -250,3 +252,39 @@ def test_append_half_step_ties(bits):
     pool = w.cache.own_pool(0, 0).cpu().numpy()
     ref = O.pack_pool(bits, 32, qh, w.page_table_np, w.num_pages, 128)
     assert np.array_equal(pool, ref)
+
+
+def test_decode_argument_errors():
+    """Each invalid decode argument is an error status before anything is enqueued: tau negative
+    or not finite, a negative or non-finite score scale, split_tokens not a multiple of 32, a
+    mask row shorter than the context, more splits than the workspace holds, a batch above the
+    shape's, a cell outside the plan. The output buffer stays untouched."""
+    w = Workload([[4]], batch=2, lens=[64, 64], seed=53, max_splits=2, stride_extra=2)
+    w.append_upto(w.lens)
+    q = synth.queries(2, 16, 128, 53).cuda()
+    seq = w.seq_lens(0, 0)
+    out = torch.full((2, 16, 128), 7.0, dtype=torch.float32, device="cuda")
+    ctx = w.page_table_np.shape[1] * 32
+    mask = torch.zeros((2, 16, ctx), dtype=torch.uint8, device="cuda")
+
+    def call(layer=0, loop=0, batch=2, **o):
+        opts = L.DecodeOpts(o.get("tau", 0.0), o.get("sm", 0.0), o.get("split", 0), o.get("stride", 0),
+                            None, o.get("mask"), None, 0)
+        L.loopkv_decode_attention(w.cache.handle, layer, loop, q.data_ptr(), batch, seq.data_ptr(),
+                                  w.page_table.data_ptr(), w.page_table.stride(0), opts, out.data_ptr(), 0)
+
+    cases = [(dict(tau=-0.1), L.EINVAL), (dict(tau=math.nan), L.EINVAL), (dict(tau=math.inf), L.EINVAL),
+             (dict(sm=-1.0), L.EINVAL), (dict(sm=math.nan), L.EINVAL), (dict(split=48), L.EINVAL),
+             (dict(split=-32), L.EINVAL), (dict(mask=mask.data_ptr(), stride=ctx - 1), L.EINVAL),
+             (dict(split=32), L.ECAPACITY), (dict(batch=3), L.EINVAL), (dict(batch=0), L.EINVAL),
+             (dict(layer=1), L.EINVAL), (dict(loop=1), L.EINVAL), (dict(loop=-1), L.EINVAL)]
+    for kw, status in cases:
+        with pytest.raises(L.LoopKVError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0) and torch.all(mask == 0)
+    call(split=32 * (ctx // 64 + 1))                 # two splits: within the workspace
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(out)) and not torch.all(out == 7.0)
+    assert w.cache.device_errors() == 0
