@@ -288,3 +288,31 @@ def test_decode_argument_errors():
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(out)) and not torch.all(out == 7.0)
     assert w.cache.device_errors() == 0
+
+
+def test_append_argument_errors():
+    """Invalid append arguments are error statuses with nothing enqueued (a batch above the
+    shape's, more new tokens than a row can hold, a cell outside the plan, a null pointer), and
+    n_new == 0 is a no-op."""
+    w = Workload([[4]], batch=2, lens=[64, 64], seed=54)
+    w.append_upto([40, 40])
+    before = [w.cache.own_pool(0, 0).clone(), *[t.clone() for t in w.cache.tail(0, 0)],
+              w.cache.qgroups(0, 0).clone()]
+    cap = w.page_table_np.shape[1] * 32
+    kk = torch.zeros(3, cap + 32, 16, 128, dtype=torch.bfloat16, device="cuda")
+    seq = w.seq_lens(0, 0)
+
+    def call(layer=0, loop=0, batch=2, n_new=1, k=kk.data_ptr(), lens=seq.data_ptr()):
+        L.loopkv_quantize_append(w.cache.handle, layer, loop, k, kk.data_ptr(), batch, n_new, None, lens,
+                                 w.page_table.data_ptr(), w.page_table.stride(0), 0)
+
+    for kw in [dict(batch=3), dict(batch=0), dict(n_new=cap + 1), dict(n_new=-1), dict(layer=1),
+               dict(loop=1), dict(k=None), dict(lens=None)]:
+        with pytest.raises(L.LoopKVError) as e:
+            call(**kw)
+        assert e.value.status == L.EINVAL, kw
+    call(n_new=0)
+    torch.cuda.synchronize()
+    after = [w.cache.own_pool(0, 0), *w.cache.tail(0, 0), w.cache.qgroups(0, 0)]
+    assert all(torch.equal(a, b) for a, b in zip(before, after))
+    assert w.cache.device_errors() == 0
