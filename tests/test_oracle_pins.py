@@ -539,3 +539,83 @@ def test_planner_monotone_in_budgets():
         if prev is not None:
             assert c[2] <= prev
         prev = c[2]
+
+
+# --------------------------------------------------------------------------------------
+# End to end against a scalar pure-Python decode (no NumPy in the computation)
+# --------------------------------------------------------------------------------------
+def _half(x):
+    """Nearest fp16 value of a Python float, ties to even (struct's 'e' format rounds so)."""
+    import struct
+    return struct.unpack("<e", struct.pack("<e", x))[0]
+
+
+def _scalar_quant(xs, bits):
+    levels = (1 << bits) - 1
+    mn, mx = min(xs), max(xs)
+    s, z = _half((mx - mn) / levels), _half(mn)
+    codes = [0 if s == 0 else min(max(math.floor((x - z) / s + 0.5), 0), levels) for x in xs]
+    return codes, s, z
+
+
+def _scalar_decode(q, k, v, tail_k, tail_v, bits, v_group, sm, tau, m0, split):
+    """Quantize (keys per channel over 32-token groups, values per token over v_group channels),
+    dequantize (cold 4-bit values at the middle of their high-plane bucket), stream the fetch
+    test (running maximum per split, updated per group before its tokens are tested), softmax
+    over history and exact tail, weighted sum of values. Lists and loops only."""
+    n, d = len(k), len(q)
+    khat = [[0.0] * d for _ in range(n)]
+    for g0 in range(0, n, 32):
+        for c in range(d):
+            codes, s, z = _scalar_quant([k[t][c] for t in range(g0, g0 + 32)], bits)
+            for i, t in enumerate(range(g0, g0 + 32)):
+                khat[t][c] = s * codes[i] + z
+    vfull, vcold = [[0.0] * d for _ in range(n)], [[0.0] * d for _ in range(n)]
+    for t in range(n):
+        for c0 in range(0, d, v_group):
+            codes, s, z = _scalar_quant(v[t][c0:c0 + v_group], bits)
+            for i, c in enumerate(range(c0, c0 + v_group)):
+                vfull[t][c] = s * codes[i] + z
+                vcold[t][c] = s * (4 * (codes[i] >> 2) + 1.5) + z
+    score = [sm * sum(q[c] * khat[t][c] for c in range(d)) for t in range(n)]
+    hot = [True] * n
+    if bits == 4:
+        span = split if split else n
+        for a in range(0, n, span):
+            m = m0
+            for g0 in range(a, min(a + span, n), 32):
+                m = max(m, max(score[g0:g0 + 32]))
+                for t in range(g0, g0 + 32):
+                    hot[t] = math.exp(score[t] - m) >= tau
+    vals = [vfull[t] if hot[t] else vcold[t] for t in range(n)] + [list(r) for r in tail_v]
+    allsc = score + [sm * sum(q[c] * r[c] for c in range(d)) for r in tail_k]
+    mx = max(allsc)
+    w = [math.exp(x - mx) for x in allsc]
+    tot = sum(w)
+    out = [sum(w[j] * vals[j][c] for j in range(len(w))) / tot for c in range(d)]
+    return out, hot
+
+
+@pytest.mark.parametrize("bits,tau,split,m0", [(4, 0.05, 0, -math.inf), (4, 0.2, 64, -math.inf),
+                                               (4, 0.01, 32, 0.8), (2, 0.05, 0, -math.inf)])
+def test_decode_matches_scalar_python(bits, tau, split, m0):
+    """The whole oracle decode (quantize, dequantize, fetch mask, softmax attention) against the
+    scalar loops above on tiny rows (D = 8, 8-channel value groups, 96 history tokens and 5 exact
+    ones): the hot set exactly, the output to 1e-12 relative. Intermediate tau values, so hot
+    and cold tokens mix in the output."""
+    rng = np.random.default_rng(900 + bits + int(tau * 1000) + split)
+    d, n = 8, 96
+    k = np.round(rng.normal(size=(n, d)) * 64) / 64
+    k[:, 3] *= 6.0                              # one outlier channel concentrates attention
+    v = np.round(rng.normal(size=(n, d)) * 64) / 64
+    tk, tv = np.round(rng.normal(size=(5, d)) * 64) / 64, np.round(rng.normal(size=(5, d)) * 64) / 64
+    q = np.round(rng.normal(size=d) * 64) / 64
+    sm = 1 / math.sqrt(d)
+    ref, hot_ref = _scalar_decode(q.tolist(), k.tolist(), v.tolist(), tk.tolist(), tv.tolist(),
+                                  bits, 8, sm, tau, m0, split)
+    qh = O.quantize_head(k, v, bits, 8)
+    out, hot, _ = O.decode_head(q, qh, tk, tv, sm_scale=sm, tau=tau, m0=m0, split_tokens=split)
+    assert list(hot) == hot_ref
+    if bits == 4:
+        assert 0 < sum(hot_ref) < n                  # both kinds of token present
+    assert np.allclose(out, ref, rtol=0, atol=1e-12 * max(abs(x) for x in ref))
