@@ -316,3 +316,23 @@ def test_append_argument_errors():
     after = [w.cache.own_pool(0, 0), *w.cache.tail(0, 0), w.cache.qgroups(0, 0)]
     assert all(torch.equal(a, b) for a, b in zip(before, after))
     assert w.cache.device_errors() == 0
+
+
+@pytest.mark.parametrize("split", [0, 128])
+def test_decode_repeats_bit_identical(split):
+    """The same decode call, repeated, gives bit-identical outputs and fetch masks: the kernels
+    combine waves and splits in a fixed order and take no data-dependent schedule."""
+    plan = np.array([[4], [2], [0], [4]], np.uint8)
+    w = Workload(plan, batch=4, lens=[700, 333, 1000, 64], seed=61)
+    w.append_upto(w.lens, chunk=256)
+    for t in range(4):
+        q = synth.queries(4, 16, 128, 610 + t).cuda()
+        res = []
+        for _ in range(3):
+            mask = _mask_buf(w)
+            out = w.cache.decode(0, t, q, w.seq_lens(t, 0), w.page_table, tau=0.02, split_tokens=split,
+                                 fetch_mask=mask)
+            res.append((out.clone(), mask.clone()))
+        for o, m in res[1:]:
+            assert torch.equal(o, res[0][0]) and torch.equal(m, res[0][1]), f"loop {t} split {split}"
+    assert w.cache.device_errors() == 0
