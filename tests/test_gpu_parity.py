@@ -202,14 +202,15 @@ def test_decode_value_groups(v_group):
     assert w.cache.device_errors() == 0
 
 
-@pytest.mark.parametrize("heads,batch", [(1, 3), (6, 3), (20, 52)])
+@pytest.mark.parametrize("heads,batch", [(1, 3), (6, 3), (20, 52), (4, 1100)])
 def test_decode_head_counts(heads, batch):
-    """Head counts off the 16-head shape: 1 and 6 heads (one head per workgroup) and 20 heads x
+    """Head counts off the 16-head shape: 1 and 6 heads (one head per workgroup), 20 heads x
     52 requests (260 four-head workgroups on 256 CUs: more than one generation, so requests are
-    taken longest first). Plan [4, 2, REUSE, 4], ragged lengths, tau 0.02."""
+    taken longest first), and 4 heads x 1100 requests (above the batch the longest-first order
+    covers: launch order). Plan [4, 2, REUSE, 4], ragged lengths, tau 0.02."""
     plan = np.array([[4], [2], [0], [4]], np.uint8)
     rng = np.random.default_rng(300 + heads)
-    lens = rng.integers(33, 230, size=batch).astype(np.int32)
+    lens = rng.integers(33, 230 if batch < 1000 else 100, size=batch).astype(np.int32)
     log(f"decode heads={heads} batch={batch}")
     w = Workload(plan, batch=batch, lens=lens, heads=heads, seed=91 + heads)
     w.append_upto(w.lens, chunk=100)
