@@ -337,3 +337,26 @@ def test_decode_repeats_bit_identical(split):
         for o, m in res[1:]:
             assert torch.equal(o, res[0][0]) and torch.equal(m, res[0][1]), f"loop {t} split {split}"
     assert w.cache.device_errors() == 0
+
+
+def test_fetch_mask_contents_int2_and_tail():
+    """The fetch mask as the header states it: 1 for every history token of a cell read at 2 bits,
+    0 or 1 for a 4-bit cell's history, and the tail's entries (tokens not yet quantized) left as
+    they were."""
+    plan = np.array([[2, 4]], np.uint8)          # one loop, two layers: INT2 and INT4
+    lens = np.array([100, 45, 257], np.int32)
+    w = Workload(plan, batch=3, lens=lens, seed=63)
+    w.append_upto(w.lens, chunk=50)
+    q = synth.queries(3, 16, 128, 630).cuda()
+    for layer, bits in [(0, 2), (1, 4)]:
+        mask = _mask_buf(w)
+        w.cache.decode(layer, 0, q, w.seq_lens(0, layer), w.page_table, tau=0.02, fetch_mask=mask)
+        mk = mask.cpu().numpy()
+        for b, n in enumerate(lens):
+            hist = (int(n) // 32) * 32
+            if bits == 2:
+                assert (mk[b, :, :hist] == 1).all()
+            else:
+                assert np.isin(mk[b, :, :hist], [0, 1]).all()
+            assert (mk[b, :, hist:] == 0xEE).all(), (layer, b)
+    assert w.cache.device_errors() == 0
