@@ -360,3 +360,37 @@ def test_fetch_mask_contents_int2_and_tail():
                 assert np.isin(mk[b, :, :hist], [0, 1]).all()
             assert (mk[b, :, hist:] == 0xEE).all(), (layer, b)
     assert w.cache.device_errors() == 0
+
+
+def test_stats_counters_match_oracle():
+    """The optional counters as the header defines them, accumulated over two calls: history
+    (token, head) pairs read, those whose low plane was read (the oracle's hot count, up to tokens
+    within the tau tie band), pairs read from 4-bit pools, and exact pairs."""
+    plan = np.array([[2, 4]], np.uint8)
+    lens = np.array([300, 129, 64], np.int32)
+    w = Workload(plan, batch=3, lens=lens, seed=64)
+    w.append_upto(w.lens, chunk=100)
+    q = synth.queries(3, 16, 128, 640)
+    hist = sum((int(n) // 32) * 32 for n in lens) * 16
+    exact = sum(int(n) % 32 for n in lens) * 16
+    for layer, bits in [(0, 2), (1, 4)]:
+        st = torch.zeros(4, dtype=torch.int64, device="cuda")
+        for _ in range(2):
+            w.cache.decode(layer, 0, q.cuda(), w.seq_lens(0, layer), w.page_table, tau=0.02, stats=st)
+        s = st.cpu().numpy().tolist()
+        assert s[0] == 2 * hist and s[3] == 2 * exact
+        if bits == 2:
+            assert s[1] == 0 and s[2] == 0
+        else:
+            _, hot = w.oracle_decode(0, layer, q, tau=0.02)
+            n_hot = sum(int(h.sum()) for row in hot for h in row)
+            qh = w.quant(0, layer, w.hist(0, layer))
+            q64 = to64(q)
+            n_tie = 0
+            for b in range(3):
+                for h in range(16):
+                    kh = O.dequant_keys(qh[b][h].k_codes, qh[b][h].k_s, qh[b][h].k_z)
+                    n_tie += int(O.tie_mask((kh @ q64[b, h]) / np.sqrt(128.0), -np.inf, 0.02, 0).sum())
+            assert s[2] == 2 * hist
+            assert abs(s[1] - 2 * n_hot) <= 2 * n_tie, (s[1], 2 * n_hot, n_tie)
+    assert w.cache.device_errors() == 0
