@@ -16,11 +16,15 @@ stores each as an fp16.
 Functions and what pins them (tests/test_oracle_pins.py):
   quantize_keys / quantize_values  -- closed-form ramps, constant groups, brute-force
                                       nearest-grid search, the half-step error bound
-  split_planes / dequant_*          -- bijection c = 4*hi + lo, cold error (1.5 - lo)*s
+  split_planes / dequant_*          -- bijection c = 4*hi + lo, cold error (1.5 - lo)*s,
+                                      cold value = the nearest 2-bit grid point (bucket middle)
   fetch_mask                        -- tau=0 all hot, tau>1 all cold, conservativeness
                                       against the global row max (Proposition 1's proof),
                                       a non-streaming brute force on tiny rows (also with
                                       the history starting after a sink)
+  tie_mask                          -- hand-placed scores at exp(s - m) = tau +- 5e-7 (ties)
+                                      and tau +- 2e-6 (not), within a split, across a split
+                                      reset, after a sink; rare on benchmark-like scores
   near_far_split                    -- token-by-token enumeration of the window rule
   decode_head with a sink           -- library attention over sink + history + window,
                                       closed-form all-cold row under a dominant sink,
@@ -29,6 +33,8 @@ Functions and what pins them (tests/test_oracle_pins.py):
                                       tau=0 and tau>1, one token, zero query, the
                                       Proposition-1 error bound, split and page invariance
   pack_head_block / unpack          -- round trip, hand-placed single codes
+  pack_pool                         -- hand-derived byte positions of head blocks > 0 in
+                                      shuffled pages, history after a 32-token sink
   cache_bytes_ref                   -- the paper's KiB-per-token figures (32-channel
                                       value groups)
   plan_exhaustive / plan_milp       -- each other (enumeration of every plan vs an integer

@@ -21,7 +21,7 @@ import oracle as O
 from quantized_kv_decode_amd import loopkv as L
 from quantized_kv_decode_amd import synth
 from quantized_kv_decode_amd.cache import LoopKVCache
-from tests.helpers import OUT_RTOL, check_mask, log
+from tests.helpers import assert_ties_rare, OUT_RTOL, check_mask, log
 
 pytestmark = pytest.mark.gpu
 
@@ -103,7 +103,7 @@ def _run_case(name, *, B, lens, P, split, heavy, seed, rows_per_cell, append_one
         out = out.cpu().double().numpy()
         mk = mask.cpu().numpy()
         q64 = q.float().double().numpy()
-        errs, refmax, ties = 0.0, 0.0, 0
+        errs, refmax, ties, compared = 0.0, 0.0, 0, 0
         for (b, h) in sample:
             n = int(lens[b])
             # sink [0, se), quantized history [S, he), exact tail [he, n)
@@ -120,6 +120,8 @@ def _run_case(name, *, B, lens, P, split, heavy, seed, rows_per_cell, append_one
                 m0 = float((kt[:se] @ q64[b, h]).max()) / math.sqrt(D) if se else -math.inf
                 tie = O.tie_mask(s, m0, tau, split, start=S)
                 ties += check_mask(mk[b, h, S:], hot, tie, f"[{name}] loop {t} b={b} h={h}")
+                compared += hot.shape[0]
+        assert_ties_rare(ties, compared, f"[{name}] loop {t}")
         log(f"[{name}] loop {t}: max err {errs:.3e}, max |ref| {refmax:.3e}, ties {ties}")
         assert errs <= OUT_RTOL * refmax, f"[{name}] loop {t}: {errs:.3e} > {OUT_RTOL} * {refmax:.3e}"
     assert cache.device_errors() == 0

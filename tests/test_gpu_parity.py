@@ -12,7 +12,7 @@ import torch
 import oracle as O
 from quantized_kv_decode_amd import loopkv as L
 from quantized_kv_decode_amd import synth
-from tests.helpers import Workload, check_mask, check_out, log, to64
+from tests.helpers import assert_ties_rare, Workload, check_mask, check_out, log, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -393,4 +393,5 @@ def test_stats_counters_match_oracle():
                     n_tie += int(O.tie_mask((kh @ q64[b, h]) / np.sqrt(128.0), -np.inf, 0.02, 0).sum())
             assert s[2] == 2 * hist
             assert abs(s[1] - 2 * n_hot) <= 2 * n_tie, (s[1], 2 * n_hot, n_tie)
+            assert_ties_rare(n_tie, hist, "stats test")
     assert w.cache.device_errors() == 0

@@ -138,13 +138,67 @@ def _token_bytes_no_ksz(bits, d=128, v_group=128, k_group=32):
     return r
 
 
+def _tie_band_x1000(scores, m0, tau, split_tokens=0, group=32, band=1e-6, start=0):
+    return M.__dict__["_orig_tie_mask"](scores, m0, tau, split_tokens, group, band * 1000, start)
+
+
+def _tie_no_split_reset(scores, m0, tau, split_tokens=0, group=32, band=1e-6, start=0):
+    return M.__dict__["_orig_tie_mask"](scores, m0, tau, 0, group, band, start)
+
+
+def _tie_splits_from_history_start(scores, m0, tau, split_tokens=0, group=32, band=1e-6, start=0):
+    return M.__dict__["_orig_tie_mask"](scores, m0, tau, split_tokens, group, band, 0)
+
+
+def _tie_band_log_units(scores, m0, tau, split_tokens=0, group=32, band=1e-6, start=0):
+    scores = np.asarray(scores, dtype=np.float64)
+    tie = np.zeros(scores.shape[0], dtype=bool)
+    m = m0
+    for g0, g1, new_split in M._split_groups(scores.shape[0], start, split_tokens, group):
+        if new_split:
+            m = m0
+        m = max(m, float(scores[g0:g1].max()))
+        tie[g0:g1] = np.abs(scores[g0:g1] - m - math.log(tau)) <= band
+    return tie
+
+
+def _tie_own_group_max(scores, m0, tau, split_tokens=0, group=32, band=1e-6, start=0):
+    scores = np.asarray(scores, dtype=np.float64)
+    tie = np.zeros(scores.shape[0], dtype=bool)
+    for g0, g1, _ in M._split_groups(scores.shape[0], start, split_tokens, group):
+        m = max(m0, float(scores[g0:g1].max()))
+        tie[g0:g1] = np.abs(np.exp(scores[g0:g1] - m) - tau) <= band
+    return tie
+
+
+def _pack_pool_ignores_sink(bits, page_tokens, heads_q, page_table, num_pages, v_group=128, hist_start=0):
+    return M.__dict__["_orig_pack_pool"](bits, page_tokens, heads_q, page_table, num_pages, v_group, 0)
+
+
+def _pack_pool_heads_reversed(bits, page_tokens, heads_q, page_table, num_pages, v_group=128, hist_start=0):
+    rev = [list(reversed(row)) for row in heads_q]
+    return M.__dict__["_orig_pack_pool"](bits, page_tokens, rev, page_table, num_pages, v_group, hist_start)
+
+
 MUTANTS = {
+    "pool pages placed from token 0 despite a sink": ("pack_pool", _pack_pool_ignores_sink,
+                                                      [P.test_pool_placement_fixture], []),
+    "pool head blocks in reverse order": ("pack_pool", _pack_pool_heads_reversed,
+                                          [P.test_pool_placement_fixture], []),
+    "tie band 1000x too wide": ("tie_mask", _tie_band_x1000, [P.test_tie_mask_hand_placed], [0.01]),
+    "tie band without the per-split reset": ("tie_mask", _tie_no_split_reset,
+                                             [P.test_tie_mask_hand_placed], [0.01]),
+    "tie band splits counted from the history start": ("tie_mask", _tie_splits_from_history_start,
+                                                       [P.test_tie_mask_hand_placed], [0.02]),
+    "tie band in log units": ("tie_mask", _tie_band_log_units, [P.test_tie_mask_hand_placed], [0.01]),
+    "tie band against the group's own maximum": ("tie_mask", _tie_own_group_max,
+                                                 [P.test_tie_mask_hand_placed], [0.01]),
     "round half dropped": ("_quantize", _quantize_no_half,
                            [P.test_quantize_matches_nearest_grid_point, P.test_quantize_ramp_closed_form], [4]),
     "scale over 2^b levels": ("_quantize", _quantize_scale_by_levels_plus_one,
                               [P.test_quantize_ramp_closed_form], [4]),
     "planes swapped": ("split_planes", _planes_swapped, [P.test_planes_bijection_and_cold_error], []),
-    "cold midpoint 2": ("dequant_values_cold", _cold_midpoint_2, [P.test_planes_bijection_and_cold_error], []),
+    "cold midpoint 2": ("dequant_values_cold", _cold_midpoint_2, [P.test_cold_value_is_nearest_bucket_midpoint], []),
     "cold test <=": ("fetch_mask", _mask_le, [P.test_mask_matches_non_streaming_brute_force], [0, 1.0, 0.5]),
     "max joined after test": ("fetch_mask", _mask_max_after_test,
                               [P.test_mask_matches_non_streaming_brute_force], [0, 0.02, -math.inf]),
@@ -180,6 +234,8 @@ def test_pins_catch_mutant(name, monkeypatch):
     monkeypatch.setitem(M.__dict__, "_orig_token_head_bytes", M.token_head_bytes)
     monkeypatch.setitem(M.__dict__, "_orig_decode_head", M.decode_head)
     monkeypatch.setitem(M.__dict__, "_orig_plan_cost", M.plan_cost)
+    monkeypatch.setitem(M.__dict__, "_orig_tie_mask", M.tie_mask)
+    monkeypatch.setitem(M.__dict__, "_orig_pack_pool", M.pack_pool)
     monkeypatch.setattr(M, attr, mutant)
     monkeypatch.setattr(O, attr, mutant, raising=False)
     caught = []

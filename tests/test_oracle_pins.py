@@ -194,6 +194,92 @@ def test_mask_identities_and_conservativeness():
                           O.fetch_mask(scores, -math.inf, 0.05, 4096))
 
 
+
+def _tie_case(tau, m, offsets):
+    """Scores whose test value exp(s - m) sits at tau + offset for a known running maximum m."""
+    return [m + math.log(tau + o) for o in offsets]
+
+
+@pytest.mark.parametrize("tau", [0.01, 0.02])
+def test_tie_mask_hand_placed(tau):
+    """Tokens placed at exp(s - m) = tau +- 5e-7 are ties, tokens at tau +- 2e-6 are not: within
+    one split, after a split reset (the second split's maximum starts again at the seed), and
+    with the history starting after a 32-token sink (splits still count from token 0)."""
+    far = -40.0                                   # exp(far - m) is nowhere near tau
+    # one split, seed below the group maximum 0
+    s = np.full(128, far)
+    s[0] = 0.0
+    s[3:7] = _tie_case(tau, 0.0, [5e-7, -5e-7, 2e-6, -2e-6])
+    s[40:42] = _tie_case(tau, 0.0, [-4e-7, 1.5e-6])   # a later group: the maximum is still 0
+    t = O.tie_mask(s, -math.inf, tau, 0)
+    assert set(np.nonzero(t)[0]) == {3, 4, 40}
+    # a seed above every score sets the maximum
+    s2 = np.full(64, far)
+    s2[10:13] = _tie_case(tau, 2.5, [3e-7, -9e-7, 3e-6])
+    assert set(np.nonzero(O.tie_mask(s2, 2.5, tau, 0))[0]) == {10, 11}
+    # split reset: 64-token splits, the second split's largest score is -3
+    s3 = np.full(128, far)
+    s3[0] = 0.0
+    s3[64] = -3.0
+    s3[70:72] = _tie_case(tau, -3.0, [5e-7, 2e-6])
+    s3[72] = math.log(tau + 5e-7)                 # a tie only against the first split's maximum
+    s3[20] = math.log(tau - 5e-7)                 # a tie in the first split
+    assert set(np.nonzero(O.tie_mask(s3, -math.inf, tau, 64))[0]) == {20, 70}
+    # history after a sink: history token j is token 32 + j; 64-token splits from token 0 put
+    # history group 0 (tokens 32..63) in split 0 and history group 1 (64..95) in split 1
+    s4 = np.full(96, far)
+    s4[0] = 0.0
+    s4[32] = -3.0
+    s4[40:42] = _tie_case(tau, -3.0, [5e-7, -2e-6])
+    s4[15] = math.log(tau - 5e-7)                 # history group 0, maximum 0
+    assert set(np.nonzero(O.tie_mask(s4, -math.inf, tau, 64, start=32))[0]) == {15, 40}
+    # the tie band covers both sides of every fetch decision the kernel could take differently
+    for sc, m0, sp, st in [(s, -math.inf, 0, 0), (s3, -math.inf, 64, 0), (s4, -math.inf, 64, 32)]:
+        hot = O.fetch_mask(sc, m0, tau, sp, start=st)
+        tie = O.tie_mask(sc, m0, tau, sp, start=st)
+        assert hot[tie].any() and (~hot[tie]).any()
+
+
+def test_tie_band_is_rare_on_benchmark_like_scores():
+    """On scores of the benchmark's distribution the tie band holds well under 1e-4 of the
+    tokens, so excluding it from the mask comparison leaves the comparison nearly complete."""
+    rng = np.random.default_rng(12)
+    n_tie = n = 0
+    for trial in range(64):
+        k, _, qh = _head(rng, 1024, 4)
+        q = rand_bf16(rng, 128)
+        sc = (O.dequant_keys(qh.k_codes, qh.k_s, qh.k_z) @ q) / math.sqrt(128)
+        for tau in [0.005, 0.01, 0.02]:
+            n_tie += int(O.tie_mask(sc, -math.inf, tau, [0, 256][trial % 2]).sum())
+            n += sc.size
+    assert n_tie <= 1e-4 * n
+
+
+# ------------------------------------------------------------------ cold value = 2-bit rounding
+def test_cold_value_is_nearest_bucket_midpoint():
+    """A cold INT4 token decodes to the middle of its high-plane bucket, which is the point of
+    the 2-bit grid {1.5, 5.5, 9.5, 13.5} (in 4-bit steps) nearest to its 4-bit code: the
+    high-plane dequantization is the 2-bit rounding of the 4-bit code."""
+    mids = np.array([1.5, 5.5, 9.5, 13.5])
+    rng = np.random.default_rng(13)
+    s = O.fp16_rne(rng.uniform(0.01, 3, size=(16, 1)))
+    z = O.fp16_rne(rng.standard_normal((16, 1)))
+    codes = np.tile(np.arange(16), (16, 8))          # every code, every channel position
+    cold = O.dequant_values_cold(codes, s, z)
+    for c in range(16):
+        d = np.abs(c - mids)
+        nearest = mids[np.argmin(d)]
+        assert np.sum(d == d.min()) == 1              # never a tie between two midpoints
+        sel = codes == c
+        assert np.all(cold[sel] == (np.broadcast_to(s, codes.shape) * nearest
+                                    + np.broadcast_to(z, codes.shape))[sel])
+    # and in value terms: the cold value is the nearest point of the 2-bit grid z + s*(1.5 + 4k)
+    full = O.dequant_values_full(codes, s, z)
+    grid = z[:, :, None] + s[:, :, None] * mids[None, None, :]
+    pick = np.take_along_axis(grid.repeat(codes.shape[1], 1),
+                              np.argmin(np.abs(full[:, :, None] - grid), axis=2)[:, :, None], 2)[:, :, 0]
+    assert np.allclose(cold, pick, rtol=1e-15, atol=0)
+
 # ------------------------------------------------------------------ attention
 def _sdpa(q, k, v):
     """torch's scaled-dot-product attention in float64 (library routine, default 1/sqrt(D))."""
@@ -300,6 +386,36 @@ def test_layout_fixture_positions():
         expect = case.get("bytes", [[case.get("byte"), case.get("value")]])
         nz = {int(i): int(buf[i]) for i in np.nonzero(buf)[0]}
         assert nz == {b: v for b, v in expect}, case["what"]
+
+
+def test_pool_placement_fixture():
+    """pack_pool puts each head block of each history page where the page table and the head
+    index say, with the history starting after a 32-token sink (hand-derived positions)."""
+    fx = json.load(open(os.path.join(GOLDEN, "pool_placement.json")))
+    for case in fx["cases"]:
+        bits, P, H, B, n = case["bits"], case["page_tokens"], case["heads"], case["batch"], case["hist_tokens"]
+        heads = []
+        for b in range(B):
+            row = []
+            for h in range(H):
+                z = lambda *sh: np.zeros(sh)
+                qh = O.QuantHead(bits, np.zeros((n, 128), np.int64), z(n // 32, 128), z(n // 32, 128),
+                                 np.zeros((n, 128), np.int64), z(n, 1), z(n, 1))
+                for st in case["sets"]:
+                    if (st["b"], st["h"]) != (b, h):
+                        continue
+                    if st["kind"] == "k_code":
+                        qh.k_codes[st["token"], st["channel"]] = st["value"]
+                    elif st["kind"] == "v_code":
+                        qh.v_codes[st["token"], st["channel"]] = st["value"]
+                    else:
+                        qh.k_s[st["group"], st["channel"]] = st["value"]
+                row.append(qh)
+            heads.append(row)
+        pool = O.pack_pool(bits, P, heads, np.array(case["page_table"]), case["num_pages"], 128,
+                           hist_start=case["hist_start"]).reshape(-1)
+        nz = {int(i): int(pool[i]) for i in np.nonzero(pool)[0]}
+        assert nz == {b: v for b, v in case["bytes"]}, case["what"]
 
 
 @pytest.mark.parametrize("bits", [2, 4])
