@@ -204,9 +204,14 @@ def fetch_mask(scores, m0, tau, split_tokens=0, group=K_GROUP, start=0):
 
 def tie_mask(scores, m0, tau, split_tokens=0, group=K_GROUP, band=1e-6, start=0):
     """Tokens whose test value exp(s_j - m) lies within `band` of tau: their hot/cold
-    decision may differ between fp64 and a kernel's fp32 arithmetic."""
+    decision may differ between fp64 and a kernel's fp32 arithmetic.
+
+    At tau <= 0 there are none: the cold test exp(s_j - m) < tau is false for every token in
+    any precision (a weight is never negative), so no decision can differ."""
     scores = np.asarray(scores, dtype=np.float64)
     tie = np.zeros(scores.shape[0], dtype=bool)
+    if tau <= 0:
+        return tie
     m = m0
     for g0, g1, new_split in _split_groups(scores.shape[0], start, split_tokens, group):
         if new_split:

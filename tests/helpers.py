@@ -34,11 +34,12 @@ def check_out(out: torch.Tensor, ref: np.ndarray, what: str = "") -> float:
 
 
 TIE_RATE = 1e-4   # near-tau ties the mask comparison may skip, as a share of compared tokens
+TIE_FLOOR = 4     # small samples: a few ties are expected by chance (~5e-5 per token at tau 0.02)
 
 
 def assert_ties_rare(n_ties: int, n_compared: int, what: str = "") -> None:
     """The tie band excuses only a sliver of the compared fetch decisions."""
-    assert n_ties <= 1 + TIE_RATE * n_compared, f"{what}: {n_ties} ties among {n_compared} tokens"
+    assert n_ties <= TIE_FLOOR + TIE_RATE * n_compared, f"{what}: {n_ties} ties among {n_compared} tokens"
 
 
 def check_mask(mask_row: np.ndarray, hot: np.ndarray, tie: np.ndarray, what: str = "") -> int:

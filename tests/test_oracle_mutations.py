@@ -162,6 +162,18 @@ def _tie_band_log_units(scores, m0, tau, split_tokens=0, group=32, band=1e-6, st
     return tie
 
 
+def _tie_band_at_tau_zero(scores, m0, tau, split_tokens=0, group=32, band=1e-6, start=0):
+    scores = np.asarray(scores, dtype=np.float64)
+    tie = np.zeros(scores.shape[0], dtype=bool)
+    m = m0
+    for g0, g1, new_split in M._split_groups(scores.shape[0], start, split_tokens, group):
+        if new_split:
+            m = m0
+        m = max(m, float(scores[g0:g1].max()))
+        tie[g0:g1] = np.abs(np.exp(scores[g0:g1] - m) - tau) <= band
+    return tie
+
+
 def _tie_own_group_max(scores, m0, tau, split_tokens=0, group=32, band=1e-6, start=0):
     scores = np.asarray(scores, dtype=np.float64)
     tie = np.zeros(scores.shape[0], dtype=bool)
@@ -190,6 +202,8 @@ MUTANTS = {
                                              [P.test_tie_mask_hand_placed], [0.01]),
     "tie band splits counted from the history start": ("tie_mask", _tie_splits_from_history_start,
                                                        [P.test_tie_mask_hand_placed], [0.02]),
+    "tie band counting tiny weights at tau = 0": ("tie_mask", _tie_band_at_tau_zero,
+                                                  [P.test_tie_mask_hand_placed], [0.01]),
     "tie band in log units": ("tie_mask", _tie_band_log_units, [P.test_tie_mask_hand_placed], [0.01]),
     "tie band against the group's own maximum": ("tie_mask", _tie_own_group_max,
                                                  [P.test_tie_mask_hand_placed], [0.01]),

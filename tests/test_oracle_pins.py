@@ -233,6 +233,10 @@ def test_tie_mask_hand_placed(tau):
     s4[40:42] = _tie_case(tau, -3.0, [5e-7, -2e-6])
     s4[15] = math.log(tau - 5e-7)                 # history group 0, maximum 0
     assert set(np.nonzero(O.tie_mask(s4, -math.inf, tau, 64, start=32))[0]) == {15, 40}
+    # at tau = 0 every token is hot in any precision: no ties, however small the weights
+    tiny = np.array([0.0] + [-30.0] * 31)
+    assert not O.tie_mask(tiny, -math.inf, 0.0, 0).any()
+    assert O.fetch_mask(tiny, -math.inf, 0.0, 0).all()
     # the tie band covers both sides of every fetch decision the kernel could take differently
     for sc, m0, sp, st in [(s, -math.inf, 0, 0), (s3, -math.inf, 64, 0), (s4, -math.inf, 64, 32)]:
         hot = O.fetch_mask(sc, m0, tau, sp, start=st)
