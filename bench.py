@@ -35,6 +35,8 @@ WORKLOADS = {
     "ouro2.6b-192cells-b16-ctx32k": (48, 4, 16, 32768, 0.30, 0.25, 8192, True),
     "one-layer-4loops-b8-ctx4k": (1, 4, 8, 4096, None, None, 2048, False),
     "single-cell-b1-ctx256": (1, 1, 1, 256, "single", None, 64, False),
+    # batch 1: 16 rows per cell, so the library splits each row (split_tokens = LOOPKV_SPLIT_AUTO)
+    "ouro1.4b-96cells-b1-ctx8k": (24, 4, 1, 8192, 0.40, 0.25, "auto", False),
 }
 # The same caches in the paper's serving setting: a 32-token sink and a 256-token window stay
 # exact bf16 (read as 512 bytes per (token, head)), the groups between them are quantized history.
@@ -90,13 +92,18 @@ def build_cache(name, seed, tau, plan_name="seeded", v_group=128, shuffle=True, 
         plan = synth.plan(layers, loops, seed, p4, pr)
     P = 32
     pages_per_seq = N // P
+    max_splits = 64 if split == "auto" else (max(1, N // split) if split else 1)
     shape = L.make_shape(num_layers=layers, num_loops=loops, page_tokens=P, v_group=v_group, max_batch=B,
                          max_pages_per_seq=pages_per_seq, tail_tokens=64 if W == 0 else W + 64,
-                         max_splits=max(1, N // split) if split else 1, num_pages=B * pages_per_seq,
+                         max_splits=max_splits, num_pages=B * pages_per_seq,
                          sink_tokens=S, window_tokens=W)
     cache = LoopKVCache(shape, plan)
     pt_np, _ = synth.page_table([N] * B, P, seed + 1, shuffle=shuffle)
     pt = torch.as_tensor(pt_np).cuda()
+    auto = split == "auto"
+    if auto:      # the library's own choice; decode is called with LOOPKV_SPLIT_AUTO
+        split = cache.auto_split(B, pt)
+        log(f"[bench] automatic split: {split} tokens per split")
     zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
     t0 = time.time()
     for t in range(loops):
@@ -114,7 +121,7 @@ def build_cache(name, seed, tau, plan_name="seeded", v_group=128, shuffle=True, 
     # quantized history [S, he) and exact tokens (sink and window) per request
     he = max(S, (N - W) // 32 * 32)
     return cache, plan, pt, pt_np, dict(layers=layers, loops=loops, B=B, N=N, split=split, heavy=heavy,
-                                        S=S, W=W, n_hist=he - S, n_exact=N - (he - S))
+                                        S=S, W=W, n_hist=he - S, n_exact=N - (he - S), auto_split=auto)
 
 
 def knapsack_plan(name, layers, loops, seed, v_group):
@@ -536,7 +543,7 @@ def run_paged(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(graph_ms if graph_ms is not None else float(step_ms[med]), 4),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-        "dtype": "u8 codes, fp16 scales, f32 math",
+        "dtype": "u8 codes; fp16 scales and value weights; f32 scores and accumulation",
         "data": "synthetic (seeded Gaussian K/V/q, 4 outlier key channels x10 per cell and head)",
         "config": {"workload": PAGED, "layers": layers, "loops": loops, "cells": ncell, "kv_heads": H,
                    "head_dim": D, "batch": B, "context": "uniform 1024..16384 per request",
@@ -603,6 +610,8 @@ def main():
                                               shuffle=args.pages == "shuffled", split_override=args.split)
     loops, layers = plan.shape
     B, N, split = cfg["B"], cfg["N"], cfg["split"]
+    from quantized_kv_decode_amd import loopkv as L
+    call_split = L.SPLIT_AUTO if cfg["auto_split"] else split   # what each decode call passes
     ncell = loops * layers
     qs = [synth.queries(B, 16, 128, 777 + t * 100 + l, device="cuda") for t in range(loops) for l in range(layers)]
     outs = [torch.empty(B, 16, 128, dtype=torch.float32, device="cuda") for _ in range(ncell)]
@@ -610,7 +619,7 @@ def main():
 
     # Hot fractions (one pass with device counters, untimed).
     stats = torch.zeros(ncell, 4, dtype=torch.int64, device="cuda")
-    run_step(cache, plan, qs, outs, seq, pt, args.tau, split, stats=[stats[i] for i in range(ncell)])
+    run_step(cache, plan, qs, outs, seq, pt, args.tau, call_split, stats=[stats[i] for i in range(ncell)])
     torch.cuda.synchronize()
     st = stats.cpu().numpy().astype(np.float64)
     hot_frac = np.where(st[:, 2] > 0, st[:, 1] / np.maximum(st[:, 2], 1), 0.0)
@@ -629,7 +638,7 @@ def main():
     # The library launches on torch's current stream, so its events bracket the kernels.
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        run_step(cache, plan, qs, outs, seq, pt, args.tau, split)
+        run_step(cache, plan, qs, outs, seq, pt, args.tau, call_split)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ncell + 1)] for _ in range(args.steps)]
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if args.workload in FLUSHED else None
@@ -641,7 +650,7 @@ def main():
     t_wall = time.perf_counter()
     for i in range(args.steps):
         flush()
-        run_step(cache, plan, qs, outs, seq, pt, args.tau, split, events=ev[i], stream=stream)
+        run_step(cache, plan, qs, outs, seq, pt, args.tau, call_split, events=ev[i], stream=stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     step_ms = np.array([ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)])
@@ -661,8 +670,8 @@ def main():
             return all(torch.equal(a, b) for a, b in zip(outs_g, outs))
 
         graph_ms, graph_note = graph_time(
-            lambda: run_step(cache, plan, qs, outs_g, seq, pt, args.tau, split), check, args.steps,
-            advance=flush, eager_work=lambda: run_step(cache, plan, qs, outs, seq, pt, args.tau, split))
+            lambda: run_step(cache, plan, qs, outs_g, seq, pt, args.tau, call_split), check, args.steps,
+            advance=flush, eager_work=lambda: run_step(cache, plan, qs, outs, seq, pt, args.tau, call_split))
         log(f"[bench] graph: {graph_note}, {graph_ms} ms/step (eager {med_ms:.3f})")
     eager_ms = med_ms
     if graph_ms is not None and graph_ms < med_ms:   # the faster of the two launch modes
@@ -685,13 +694,23 @@ def main():
     dom = max(kinds, key=lambda b: kinds[b]["avg_us"] * kinds[b]["launches_per_step"])
     achieved = kinds[dom]["GBps"]
 
-    traffic = None
+    # HBM traffic and kernel-trace durations come from stored rocprofv3 runs of this workload
+    # (profiles/), used only while the decode sources match the ones they were taken on.
+    traffic, traffic_src, trace_us, trace_src = None, None, None, None
+    stored = (args.plan == "seeded" and args.v_group == 128 and args.split is None and args.pages == "shuffled"
+              and args.tau == 0.01)
     tfile = os.path.join(ROOT, "profiles", "decode_traffic.json")
-    if os.path.exists(tfile):
+    if stored and os.path.exists(tfile):
         tj = json.load(open(tfile))
-        if (tj.get("kernel_hash") == kernel_hash() and tj.get("workload") == args.workload
-                and args.plan == "seeded" and args.v_group == 128):
+        if tj.get("kernel_hash") == kernel_hash() and tj.get("workload") == args.workload:
             traffic = tj.get("hbm_bytes_per_launch")
+            traffic_src = f"profiles/decode_traffic.json (rocprofv3 --pmc, kernel hash {tj['kernel_hash']})"
+    kfile = os.path.join(ROOT, "profiles", "decode_kernel_trace.json")
+    if stored and os.path.exists(kfile):
+        kj = json.load(open(kfile))
+        if kj.get("kernel_hash") == kernel_hash() and kj.get("workload") == args.workload:
+            trace_us = kj.get("avg_us", {}).get(f"int{dom}_read")
+            trace_src = f"profiles/decode_kernel_trace.json (rocprofv3 --kernel-trace --stats, kernel hash {kj['kernel_hash']})"
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -708,11 +727,12 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u8 codes, fp16 scales, f32 math",
+        "dtype": "u8 codes; fp16 scales and value weights; f32 scores and accumulation",
         "data": "synthetic (seeded Gaussian K/V/q, 4 outlier key channels x10 per cell and head)",
         "config": {"workload": args.workload, "layers": layers, "loops": loops, "cells": ncell,
                    "kv_heads": 16, "head_dim": 128, "batch": B, "context": N, "tau": args.tau,
-                   "split_tokens": split, "plan_counts": {"int4": int((plan == 4).sum()),
+                   "split_tokens": split, "split_auto": cfg["auto_split"],
+                   "plan_counts": {"int4": int((plan == 4).sum()),
                                                           "int2": int((plan == 2).sum()),
                                                           "reuse": int((plan == 0).sum())},
                    "page_tokens": 32, "v_group": args.v_group, "plan": args.plan, "plan_seed": args.seed,
@@ -728,7 +748,13 @@ def main():
         "kernels": {f"decode_int{b}_read": v for b, v in kinds.items()},
         "roofline": {"bound": "hbm", "kernel": f"decode_kernel<{dom},...> (INT{dom}-read cells)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "avg_launch_us_events": kinds[dom]["avg_us"],
+                     "avg_launch_us_kernel_trace": trace_us,
+                     "frac_kernel_trace": (None if trace_us is None else
+                                           round(kinds[dom]["bytes_per_launch"] / (trace_us * 1e-6) / 1e9
+                                                 / PEAK_HBM_GBPS, 4)),
+                     "traffic_source": traffic_src, "kernel_trace_source": trace_src},
         "cpu_baseline": cpu,
         "kernel_hash": kernel_hash(),
     }

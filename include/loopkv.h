@@ -30,7 +30,9 @@
  *     validated before anything is enqueued: on any status other than LOOPKV_OK nothing has
  *     been launched. Values that live in device memory (lengths, page ids) cannot be checked
  *     on the host; kernels clamp them and record a flag readable with loopkv_device_errors.
- *   - A plan handle is not thread-safe; calls on different handles are independent.
+ *   - A plan handle is not thread-safe; calls on different handles are independent. Split
+ *     decodes of one handle share its workspace and must be ordered (see
+ *     loopkv_decode_attention).
  *   - loop and layer are 0-based; the final loop is num_loops - 1.
  */
 #ifndef LOOPKV_H
@@ -88,8 +90,9 @@ typedef struct {
   uint64_t arena_bytes;      /* total device bytes loopkv_plan_load needs */
   uint64_t pool_bytes;       /* page pools of all own-storage cells */
   uint64_t tail_bytes;       /* bf16 tail rings of all cells (REUSE cells keep their own) */
-  uint64_t meta_bytes;       /* descriptors, quantized-group counters, error word */
-  uint64_t workspace_bytes;  /* split-K partials */
+  uint64_t meta_bytes;       /* descriptors, quantized-group counters, error word, split
+                                merge counters */
+  uint64_t workspace_bytes;  /* split-K partials (the merge counters are in meta_bytes) */
   /* Bytes per token summed over every cell and head (algorithmic, excluding pool padding):
    * stored -- quantized KV kept (REUSE cells keep none);
    * read_hi_only / read_all_hot -- what one decode step reads per history token when no /
@@ -100,14 +103,19 @@ typedef struct {
   uint64_t sink_bytes;       /* bf16 sinks of all cells (REUSE cells keep their own) */
 } loopkv_bytes;
 
+/* split_tokens value that lets the library choose the split (loopkv_auto_split). */
+enum { LOOPKV_SPLIT_AUTO = -1 };
+
 /* Per-call decode options. */
 typedef struct {
   float tau;                  /* V-precision threshold; 0 fetches every low plane, > 1 none */
   float sm_scale;             /* score scale; 0 means 1/sqrt(head_dim) */
-  int32_t split_tokens;       /* 0: one split per (request, head) row; otherwise a multiple
-                                 of 32: the history is cut into runs of this many tokens
-                                 from token 0, each with its own running maximum, merged by
-                                 log-sum-exp in split order */
+  int32_t split_tokens;       /* 0: one split per (request, head) row; a multiple of 32: the
+                                 history is cut into runs of this many tokens from token 0,
+                                 each with its own running maximum, merged by log-sum-exp in
+                                 split order inside the same launch (section 3.4, "The unified
+                                 kernel": the last block of a row merges the partials);
+                                 LOOPKV_SPLIT_AUTO: the split loopkv_auto_split returns */
   int32_t mask_stride;        /* row stride of fetch_mask_dev, in bytes */
   const float* seed_dev;      /* [batch, num_q_heads] running-max seeds in score units, or
                                  NULL for -infinity */
@@ -143,7 +151,17 @@ typedef struct {
 } loopkv_cell_info;
 
 /* Sizes of the arena for `shape` and `plan` (num_loops * num_layers codes), and the
- * stored / read bytes per token. Pure host computation; no HIP call. */
+ * stored / read bytes per token. The per-token figures follow the paper's byte model:
+ * BF16 KV, KIVI-4 and the INT2 / shared-loop variants (section 2.2 "Looped transformers and
+ * their KV cache", section 3.1 C1), a shared cell storing nothing and reading its source
+ * (section 3.2 C2), the low plane counted only when read (section 3.3 C3), and the per-cell
+ * totals of Table 5; with 32-channel value groups they reproduce the paper's KiB-per-token
+ * figures exactly. out->stored_bytes_per_token excludes pool padding; arena_bytes includes
+ * every region (metadata, split workspace, rings, sinks, pools), each 256-byte aligned.
+ * Errors: LOOPKV_EINVAL (null pointer, bad shape field), LOOPKV_ENOTSUP (a shape outside the
+ * library's support), LOOPKV_EPLAN (bad plan code, REUSE in the final loop), LOOPKV_ECAPACITY
+ * (host memory exhausted). Pure host computation; no HIP call; `out` is written only on
+ * LOOPKV_OK. */
 loopkv_status loopkv_cache_bytes(const loopkv_shape* shape, const uint8_t* plan,
                                  loopkv_bytes* out);
 
@@ -159,7 +177,16 @@ loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan,
 /* Releases the handle (host memory only; the arena stays the caller's). NULL is a no-op. */
 loopkv_status loopkv_plan_free(loopkv_plan plan);
 
-/* Appends new tokens to every request of cell (layer, loop).
+/* Appends new tokens to every request of cell (layer, loop): the companion step that keeps
+ * the cache in the form decode reads. Sources: KIVI-style asymmetric quantization with fp16
+ * scale and zero point -- keys per channel over a 32-token group, values per token over
+ * v_group channels (section 5.1, "Baselines"); an INT4 cell's value codes split into a high
+ * and a low 2-bit plane (section 3.3, "Bit-plane V layout"); a page is quantized when it leaves
+ * the exact window (section 2.3, "Measuring KV damage"; section 4, "Implementation"); a shared
+ * (REUSE) cell keeps only its own exact tokens (section 3.2 C2). Codes are
+ * clamp(floor((x - z) / s + 1/2)) decided as in fp64 from the bf16 inputs; s and z are rounded
+ * to the nearest fp16 from fp64. Groups whose range exceeds the fp16 scale (a range above
+ * 65504 * (2^bits - 1)) or whose minimum exceeds the fp16 range are not representable.
  *   k_new_dev, v_new_dev: bf16 [batch, n_new, num_kv_heads, head_dim], contiguous, 16-byte
  *   aligned (LOOPKV_EINVAL otherwise).
  *   n_new_dev: optional int32 [batch]: request b appends its first n_new_dev[b] rows
@@ -198,7 +225,17 @@ loopkv_status loopkv_quantize_append(loopkv_plan plan, int32_t layer, int32_t lo
  * decode at full precision for hot tokens and to the middle of their high-plane bucket for
  * cold ones (section 3.3), with the running maximum of each split seeded by the seed joined
  * with the sink's largest score. A request with seq_len 0 gets zeros. opts may be NULL
- * (tau 0, default scale, no split). */
+ * (tau 0, default scale, no split). Every call is one kernel launch, split or not.
+ * Value range: any finite fp16 value scale (the weights are rescaled per wave by powers of
+ * two, section 3.3 keeps a scale per group); exact (bf16) sink, window and tail values must
+ * be below 2^118 in magnitude.
+ * Workspace: the split partials and the merge counters are one region of the plan's arena,
+ * so split decodes of one plan (split_tokens != 0) must not overlap in time: issue them on
+ * one stream (or order the streams), as the calls of one model step are. Errors:
+ * LOOPKV_EINVAL (null pointer, misaligned q, batch or stride out of range, tau or sm_scale
+ * negative or not finite, split_tokens not a multiple of 32 nor LOOPKV_SPLIT_AUTO, a mask
+ * stride below the context), LOOPKV_ECAPACITY (more splits than shape.max_splits),
+ * LOOPKV_EHIP (the launch failed). */
 loopkv_status loopkv_decode_attention(loopkv_plan plan, int32_t layer, int32_t loop,
                                       const void* q_dev, int32_t batch,
                                       const int32_t* seq_lens_dev,
@@ -206,6 +243,16 @@ loopkv_status loopkv_decode_attention(loopkv_plan plan, int32_t layer, int32_t l
                                       int32_t page_table_stride,
                                       const loopkv_decode_opts* opts, float* out_dev,
                                       void* stream);
+
+/* The split_tokens a decode with LOOPKV_SPLIT_AUTO uses for `batch` requests and a page table
+ * of `page_table_stride` entries (context c = min(max_pages_per_seq, stride) * page_tokens):
+ * 0 (no split) when batch * num_kv_heads rows already give every compute unit of the device
+ * a workgroup or c <= 256; otherwise about one workgroup per compute unit as splits of at
+ * least 256 tokens, at most 64 per row (section 3.4: up to 64 far blocks per decode row) and
+ * at most shape.max_splits. Deterministic for a device, so a caller (or a test) can
+ * reproduce the fetch mask. Host only. Errors: LOOPKV_EINVAL. */
+loopkv_status loopkv_auto_split(loopkv_plan plan, int32_t batch, int32_t page_table_stride,
+                                int32_t* split_tokens);
 
 /* Fills `out` with the device view of cell (layer, loop). Host only. */
 loopkv_status loopkv_get_cell_info(loopkv_plan plan, int32_t layer, int32_t loop,

@@ -79,6 +79,10 @@ class LoopKVCache:
                                   page_table.stride(0), opts, _ptr(out), _stream(stream))
         return out
 
+    def auto_split(self, batch: int, page_table: torch.Tensor) -> int:
+        """The split_tokens that split_tokens=L.SPLIT_AUTO resolves to for this batch and table."""
+        return L.loopkv_auto_split(self.handle, batch, page_table.stride(0))
+
     def cell_info(self, layer: int, loop: int) -> L.CellInfo:
         return L.loopkv_get_cell_info(self.handle, layer, loop)
 

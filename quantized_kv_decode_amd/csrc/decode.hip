@@ -10,7 +10,8 @@
 //    middle of its bucket (section 3.3, "Read-time V precision");
 //  - the per-channel key scale/zero fold into the query once per page, and the per-token value
 //    scale/zero fold into the attention weight and a running sum (Appendix, "History reader");
-//  - split partials merge by log-sum-exp, which gives the exact softmax (section 3.4).
+//  - split partials merge by log-sum-exp, which gives the exact softmax; the workgroup that
+//    finishes a row's last split does it, so every decode is one launch (section 3.4).
 //
 // Work mapping (CDNA4, wave64): one workgroup per (request, RB heads, split), NW waves per
 // (request, head) row: RB = 4 rows (16 waves, one workgroup filling a CU) when the launch
@@ -46,7 +47,14 @@ namespace loopkv {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kWScale = 256.f;        // fp16 value weights are scaled up to stay normal
+// Value weights enter the dot2 path as fp16 numbers K * p * s (p <= 1 the softmax weight, s the
+// token's fp16 value scale, K a per-wave power of two). K starts at 2^24, so every non-zero fp16
+// scale (>= 2^-24) gives weights >= p, and drops whenever a scale would push K * s past 2^15:
+// weights stay finite and normal for any fp16 scale. Exact tokens use fp32 weights with K at
+// most 2^8, which keeps their sums finite for bf16 values below 2^118.
+constexpr float kWInit = 16777216.f;     // 2^24
+constexpr float kWMax = 32768.f;         // 2^15: largest K * s
+constexpr float kWExact = 256.f;         // 2^8: largest K while exact tokens are added
 
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -340,16 +348,25 @@ __device__ __forceinline__ void load_vc(PairRegs<BITS, NVG>& g, const PairPages&
 template <int NVG>
 struct WaveState {
   float M, Lsum, m_run, W;       // W: sum of the fp16 value weights (offset of acc)
+  float K;                       // value-weight multiplier (a power of two)
   float Csum[NVG];
   // Value accumulator of channels 16*cbv + i in offset units: the high plane / INT2 codes enter
-  // through dot2 as w' * (1 + code * f_i) with w' = kWScale * weight, f_i = 1/4 (even i) or 1/16
-  // (odd i), and W collects the w'; low planes and exact tail values are added without the
-  // offset. True weighted sum of channel i = (acc[i] - W) / (f_i * kWScale).
+  // through dot2 as w' * (1 + code * f_i) with w' = K * weight and f_i = kF[i % 8], and W
+  // collects the w'; low planes and exact tail values are added without the offset. True
+  // weighted sum of channel i = (acc[i] - W) / (f_i * K).
   float acc[16];
   uint32_t lo_word[8];           // low planes of last round's hot tokens, two per lane and pass
   int nlo;                       // last round's hot count
   unsigned long long hot;
 };
+
+// Multiplies the value state (accumulators and their offset) by r, a power of two: exact.
+template <int NVG>
+__device__ __forceinline__ void scale_values(WaveState<NVG>& st, float r) {
+  st.W *= r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) st.acc[i] *= r;
+}
 
 struct RoundConst {
   float scale2, log2tau, u;
@@ -503,21 +520,36 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   }
   const int pr = rd & 1;
 
+  // ---- value-weight multiplier: K * s <= 2^15 for every value scale of this round's tokens
+  {
+    float smax = 0.f;
+    if (my_valid) {
+#pragma unroll
+      for (int i = 0; i < NVG; ++i) smax = dmax(smax, f16_lo(cur.vsz[i]));
+    }
+    if (__ballot(smax * st.K > kWMax)) {   // rare: the first rounds, or a larger scale
+      const int e = __builtin_amdgcn_frexp_expf(wave_max(smax));   // smax < 2^e
+      const float kn = __builtin_ldexpf(1.f, 15 - e);
+      scale_values(st, kn / st.K);
+      st.K = kn;
+    }
+  }
+
   // ---- per token (every lane): weight, hot/cold, value scale/zero folds
   bool hot = false;
-  _Float16 wv[NVG];   // the token's value weights (kWScale * p * s, fp16)
+  _Float16 wv[NVG];   // the token's value weights (K * p * s, fp16)
   if (my_valid) {
     const float p = fexp2(s2 - st.M);
     hot = !(k.gated && (s2 - (half ? mpreB : mpreA)) < k.log2tau);
     st.Lsum += p;
-    const float pw = p * kWScale;
+    const float pw = p * st.K;
 #pragma unroll
     for (int i = 0; i < NVG; ++i) {
       const uint32_t sz = cur.vsz[i];
       // Csum gathers p * z, plus p * 1.5 * s for a cold token (middle of its bucket)
       const float zc = (k.gated && !hot) ? fmaf(1.5f, f16_lo(sz), f16_hi(sz)) : f16_hi(sz);
       st.Csum[i] = fmaf(p, zc, st.Csum[i]);
-      // kWScale * weight, rounded to nearest fp16: the value codes and the offset W both use
+      // K * weight, rounded to nearest fp16: the value codes and the offset W both use
       // this rounded weight, and its error is unbiased (a truncated weight would bias the code
       // sum, which the zero term largely cancels in the output)
       wv[i] = (_Float16)fmaf(pw, f16_lo(sz), 0.f);
@@ -640,7 +672,7 @@ __device__ __forceinline__ float sink_wave_max(const ExactRow& x, gu16 q, float 
 // Both halves' loads are issued before the scores are formed.
 template <int NVG, int NW>
 __device__ __forceinline__ void exact_chunk(Smem<NVG, NW>& sm, WaveState<NVG>& st, const ExactRow& x,
-                                            int ch, int has_sink, float scale2, float vs_inv,
+                                            int ch, int has_sink, float scale2, float inv_vs,
                                             int w, int lane) {
   const bool is_sink = has_sink && ch == 0;
   const int cw = ch - has_sink;
@@ -707,9 +739,14 @@ __device__ __forceinline__ void exact_chunk(Smem<NVG, NW>& sm, WaveState<NVG>& s
     p[j] = fexp2(s2[j] - st.M);   // exp2(-inf) = 0 for tokens past the chunk
     psum += p[j];
   }
+  if (st.K > kWExact) {
+    scale_values(st, kWExact / st.K);
+    st.K = kWExact;
+  }
+  const float vs_inv = st.K * inv_vs;
   if (cbt == 0) {
     st.Lsum += psum;
-    // odd-channel weight in offset units: p / VS * kWScale * kF
+    // weight in offset units (before the channel's kF): p * K / VS
     float* tw = &sm.tail_w[w][tr * 8];
     *reinterpret_cast<float4*>(tw) = make_float4(p[0] * vs_inv, p[1] * vs_inv, p[2] * vs_inv, p[3] * vs_inv);
     *reinterpret_cast<float4*>(tw + 4) = make_float4(p[4] * vs_inv, p[5] * vs_inv, p[6] * vs_inv, p[7] * vs_inv);
@@ -850,6 +887,7 @@ void decode_kernel(DecodeParams prm) {
   st.M = -INFINITY;
   st.Lsum = 0.f;
   st.W = 0.f;
+  st.K = kWInit;
   st.m_run = c.seed ? c.seed[(size_t)b * H + h] * kLog2e : -INFINITY;
 
   ExactRow ex;
@@ -913,7 +951,7 @@ void decode_kernel(DecodeParams prm) {
     const int has_sink = sink_n > 0 ? 1 : 0;
     const int n_chunks = has_sink + (n_tail + kGroup - 1) / kGroup;
     for (int ch = w; ch < n_chunks; ch += NW)
-      exact_chunk<NVG, NW>(sm, st, ex, ch, has_sink, k.scale2, kWScale / VS, w, lane);
+      exact_chunk<NVG, NW>(sm, st, ex, ch, has_sink, k.scale2, 1.f / VS, w, lane);
   }
 
   // Merge the waves: sum lanes, then combine the NW softmax states.
@@ -932,8 +970,8 @@ void decode_kernel(DecodeParams prm) {
     v += __shfl_xor(v, 8);
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
-    // offset units: channel i carries code * kF[i % 8], weights x kWScale
-    acc[i] = (v - W) * (1.f / (kF[i % 8] * kWScale));
+    // offset units: channel i carries code * kF[i % 8], weights x K
+    acc[i] = (v - W) * (1.f / (kF[i % 8] * st.K));
   }
   if (lane < 8) {
 #pragma unroll
@@ -970,6 +1008,37 @@ void decode_kernel(DecodeParams prm) {
       if (tid == 0) { part[0] = Mx; part[1] = den; }
     }
   }
+  // Split partials: the workgroup that finishes a row group's last split merges them
+  // (section 3.4: the last block of a row merges the partial results by log-sum-exp), so a
+  // split decode is one launch. The counter of the row group is back at zero afterwards.
+  if (c.n_split > 1) {
+    __shared__ int s_last;
+    int* counter = c.counters + (size_t)b * H + (int)blockIdx.y * RB;
+    __threadfence();   // this thread's partials reach the device before the count
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(counter, 1) == c.n_split - 1;
+    __syncthreads();
+    if (s_last) {
+      __threadfence();   // the other workgroups' partials, not stale cached copies
+      if (tid < kHeadDim) {
+        const size_t row = (size_t)b * H + h;
+        const float* base = c.partials + row * g.max_splits * (kHeadDim + 2);
+        float Mx = -INFINITY;
+        for (int sp = 0; sp < c.n_split; ++sp) Mx = fmaxf(Mx, base[sp * (kHeadDim + 2)]);
+        float num = 0.f, den = 0.f;
+        if (Mx != -INFINITY) {
+          for (int sp = 0; sp < c.n_split; ++sp) {
+            const float* pp = base + sp * (kHeadDim + 2);
+            const float fw = pp[0] == -INFINITY ? 0.f : exp2f(pp[0] - Mx);
+            num = fmaf(fw, pp[2 + tid], num);
+            den = fmaf(fw, pp[1], den);
+          }
+        }
+        c.out[row * kHeadDim + tid] = den > 0.f ? num / den : 0.f;
+      }
+      if (threadIdx.x == 0) *counter = 0;
+    }
+  }
   if (tid == 0 && c.stats) {
     const unsigned long long nh = (unsigned long long)(ge - gs) * kGroup;
     atomicAdd(&c.stats[0], nh);
@@ -979,25 +1048,6 @@ void decode_kernel(DecodeParams prm) {
     }
     if (do_exact) atomicAdd(&c.stats[3], (unsigned long long)(n_tail + sink_n));
   }
-}
-
-// Log-sum-exp merge of the split partials of each (request, head), in split order.
-__global__ __launch_bounds__(kHeadDim) void merge_kernel(Geom g, DecodeCall c) {
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const size_t row = (size_t)b * g.H + h;
-  const float* base = c.partials + row * g.max_splits * (kHeadDim + 2);
-  float Mx = -INFINITY;
-  for (int s = 0; s < c.n_split; ++s) Mx = fmaxf(Mx, base[s * (kHeadDim + 2)]);
-  float num = 0.f, den = 0.f;
-  if (Mx != -INFINITY) {
-    for (int s = 0; s < c.n_split; ++s) {
-      const float* p = base + s * (kHeadDim + 2);
-      const float fw = p[0] == -INFINITY ? 0.f : exp2f(p[0] - Mx);
-      num = fmaf(fw, p[2 + tid], num);
-      den = fmaf(fw, p[1], den);
-    }
-  }
-  c.out[row * kHeadDim + tid] = den > 0.f ? num / den : 0.f;
 }
 
 // Waves per (request, head) row, which is also the waves per SIMD the register allocation
@@ -1040,14 +1090,9 @@ hipError_t launch_bp(const Geom& g, const DecodeCall& c, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const Geom& g, const CellDesc& dh, const DecodeCall& c, hipStream_t stream) {
-  hipError_t e;
   if (dh.read_bits == 4)
-    e = g.P == 32 ? launch_bp<4, 32>(g, c, stream) : launch_bp<4, 16>(g, c, stream);
-  else
-    e = g.P == 32 ? launch_bp<2, 32>(g, c, stream) : launch_bp<2, 16>(g, c, stream);
-  if (e != hipSuccess || c.n_split == 1) return e;
-  merge_kernel<<<dim3((unsigned)g.H, (unsigned)c.batch), kHeadDim, 0, stream>>>(g, c);
-  return hipGetLastError();
+    return g.P == 32 ? launch_bp<4, 32>(g, c, stream) : launch_bp<4, 16>(g, c, stream);
+  return g.P == 32 ? launch_bp<2, 32>(g, c, stream) : launch_bp<2, 16>(g, c, stream);
 }
 
 }  // namespace loopkv

@@ -22,6 +22,7 @@ struct loopkv_plan_s {
   CellDesc* desc_dev = nullptr;
   uint32_t* err_dev = nullptr;
   float* partials_dev = nullptr;
+  int32_t* merge_dev = nullptr;   // split counters of the in-launch merge
   int device = 0;
   int cus = 0;                    // compute units of that device
 };
@@ -87,7 +88,7 @@ loopkv_status check_plan(const loopkv_shape* s, const uint8_t* plan) {
 }
 
 struct ArenaPlan {
-  uint64_t desc_off, counters_off, err_off, partials_off, tails_off, sinks_off, pools_off, total;
+  uint64_t desc_off, counters_off, err_off, merge_off, partials_off, tails_off, sinks_off, pools_off, total;
   uint64_t tail_bytes_per_cell;  // one of K or V
   uint64_t sink_bytes_per_cell;  // one of K or V
   std::vector<uint64_t> pool_off;  // per cell; UINT64_MAX for REUSE
@@ -106,6 +107,8 @@ loopkv_status plan_arena(const loopkv_shape* s, const uint8_t* plan, ArenaPlan* 
   off = align_up(off + cells * (uint64_t)s->max_batch * sizeof(int32_t));
   a->err_off = off;
   off = align_up(off + sizeof(uint32_t));
+  a->merge_off = off;
+  off = align_up(off + (uint64_t)s->max_batch * H * sizeof(int32_t));
   const uint64_t meta = off;
   a->partials_off = off;
   if (!mul_ok((uint64_t)s->max_batch * H, (uint64_t)s->max_splits * (D + 2) * 4, &x))
@@ -178,6 +181,29 @@ Geom make_geom(const loopkv_plan_s* p) {
   return g;
 }
 
+// The split used for split_tokens = LOOPKV_SPLIT_AUTO: none when the (request, head) rows
+// alone give every compute unit a workgroup; otherwise about kAutoWgPerCu workgroups per CU,
+// as runs of at least kAutoMinSplit tokens (one round of every wave of a row), at most 64 runs
+// per row (section 3.4: up to 64 far blocks per decode row) and at most max_splits.
+constexpr int64_t kAutoWgPerCu = 1;
+constexpr int64_t kAutoMinSplit = 256;
+
+int32_t auto_split(const loopkv_plan_s* p, int32_t batch, int64_t ctx) {
+  const int64_t rows = (int64_t)batch * p->shape.num_kv_heads;
+  const int64_t cus = std::max(p->cus, 1);
+  if (rows >= cus || ctx <= kAutoMinSplit) return 0;
+  int64_t n = (kAutoWgPerCu * cus + rows - 1) / rows;
+  n = std::min<int64_t>(n, std::min<int64_t>(64, p->shape.max_splits));
+  int64_t st = (ctx + n - 1) / n;
+  st = std::max<int64_t>((st + kGroup - 1) / kGroup * kGroup, kAutoMinSplit);
+  return (ctx + st - 1) / st > 1 ? (int32_t)st : 0;
+}
+
+int64_t decode_ctx(const loopkv_plan_s* p, int32_t pt_stride) {
+  return std::min<int64_t>((int64_t)p->shape.max_pages_per_seq * p->shape.page_tokens,
+                           (int64_t)pt_stride * p->shape.page_tokens);
+}
+
 bool cell_ok(const loopkv_plan_s* p, int32_t layer, int32_t loop) {
   return p && layer >= 0 && layer < p->shape.num_layers && loop >= 0 && loop < p->shape.num_loops;
 }
@@ -240,6 +266,7 @@ loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan, v
   p->desc_dev = reinterpret_cast<CellDesc*>(base + a.desc_off);
   p->err_dev = reinterpret_cast<uint32_t*>(base + a.err_off);
   p->partials_dev = reinterpret_cast<float*>(base + a.partials_off);
+  p->merge_dev = reinterpret_cast<int32_t*>(base + a.merge_off);
   int32_t* counters = reinterpret_cast<int32_t*>(base + a.counters_off);
   p->desc.resize((size_t)T * L);
   for (int t = 0; t < T; ++t)
@@ -276,6 +303,8 @@ loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan, v
   if (e == hipSuccess)
     e = hipMemsetAsync(counters, 0, (size_t)T * L * shape->max_batch * sizeof(int32_t), s);
   if (e == hipSuccess) e = hipMemsetAsync(p->err_dev, 0, sizeof(uint32_t), s);
+  if (e == hipSuccess)
+    e = hipMemsetAsync(p->merge_dev, 0, (size_t)shape->max_batch * H * sizeof(int32_t), s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return LOOPKV_EHIP;
   *out = p.release();
@@ -286,6 +315,14 @@ loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan, v
 
 loopkv_status loopkv_plan_free(loopkv_plan plan) {
   delete plan;
+  return LOOPKV_OK;
+}
+
+loopkv_status loopkv_auto_split(loopkv_plan p, int32_t batch, int32_t page_table_stride,
+                                int32_t* split_tokens) {
+  if (!p || !split_tokens || batch < 1 || batch > p->shape.max_batch || page_table_stride < 1)
+    return LOOPKV_EINVAL;
+  *split_tokens = auto_split(p, batch, decode_ctx(p, page_table_stride));
   return LOOPKV_OK;
 }
 
@@ -354,9 +391,11 @@ loopkv_status loopkv_decode_attention(loopkv_plan p, int32_t layer, int32_t loop
   if (opts) o = *opts;
   if (!std::isfinite(o.tau) || o.tau < 0.f) return LOOPKV_EINVAL;
   if (!std::isfinite(o.sm_scale) || o.sm_scale < 0.f) return LOOPKV_EINVAL;
-  if (o.split_tokens < 0 || o.split_tokens % kGroup != 0) return LOOPKV_EINVAL;
+  if (o.split_tokens != LOOPKV_SPLIT_AUTO && (o.split_tokens < 0 || o.split_tokens % kGroup != 0))
+    return LOOPKV_EINVAL;
   const Geom g = make_geom(p);
-  const int64_t ctx = std::min<int64_t>(g.max_ctx, (int64_t)pt_stride * g.P);
+  const int64_t ctx = decode_ctx(p, pt_stride);
+  if (o.split_tokens == LOOPKV_SPLIT_AUTO) o.split_tokens = auto_split(p, batch, ctx);
   if (o.fetch_mask_dev && (int64_t)o.mask_stride < ctx) return LOOPKV_EINVAL;
   const int64_t n_split = o.split_tokens ? (ctx + o.split_tokens - 1) / o.split_tokens : 1;
   if (n_split > p->shape.max_splits) return LOOPKV_ECAPACITY;
@@ -378,6 +417,7 @@ loopkv_status loopkv_decode_attention(loopkv_plan p, int32_t layer, int32_t loop
   c.stats = o.stats_dev;
   c.out = out;
   c.partials = p->partials_dev;
+  c.counters = p->merge_dev;
   c.order_by_len = 0;   // set by the launcher from the grid size
   c.sink_seed = o.no_sink_seed ? 0 : 1;
   hipError_t e = launch_decode(g, p->desc[i], c, static_cast<hipStream_t>(stream));

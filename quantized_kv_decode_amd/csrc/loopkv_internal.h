@@ -125,6 +125,7 @@ struct DecodeCall {
   unsigned long long* stats;
   float* out;
   float* partials;        // [batch, H, max_splits, D + 2]
+  int32_t* counters;      // [batch, H]: finished splits per row group, zero between launches
   int32_t order_by_len;   // launch needs more than one generation: longest requests first
   int32_t sink_seed;      // seed the running maximum with the sink's largest score
 };

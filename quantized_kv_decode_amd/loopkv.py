@@ -15,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("LOOPKV_LIBRARY") or os.path.join(HERE, "libloopkv.so")
 
 REUSE, INT2, INT4 = 0, 2, 4
+SPLIT_AUTO = -1
 OK, EINVAL, EPLAN, ENOTSUP, ECAPACITY, EHIP, EINFEASIBLE = range(7)
 ERR_LENGTH, ERR_PAGE, ERR_TAIL = 1, 2, 4
 
@@ -68,7 +69,8 @@ class PlanCost(ctypes.Structure):
 
 SYMBOLS = ["loopkv_cache_bytes", "loopkv_plan_load", "loopkv_plan_free",
            "loopkv_quantize_append", "loopkv_decode_attention", "loopkv_get_cell_info",
-           "loopkv_device_errors", "loopkv_plan_solve", "loopkv_status_string"]
+           "loopkv_device_errors", "loopkv_plan_solve", "loopkv_auto_split",
+           "loopkv_status_string"]
 
 _lib = None
 
@@ -91,6 +93,7 @@ def lib() -> ctypes.CDLL:
         L.loopkv_device_errors.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
         L.loopkv_plan_solve.argtypes = [ctypes.POINTER(Shape), vp, ctypes.POINTER(PlanBudget), vp,
                                         ctypes.POINTER(PlanCost)]
+        L.loopkv_auto_split.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_int32)]
         L.loopkv_status_string.argtypes = [ctypes.c_int]
         L.loopkv_status_string.restype = ctypes.c_char_p
         for name in SYMBOLS:
@@ -152,6 +155,12 @@ def loopkv_decode_attention(handle, layer, loop, q_dev, batch, seq_lens_dev, pag
                                          page_table_dev, page_table_stride,
                                          ctypes.byref(opts) if opts is not None else None,
                                          out_dev, stream), "loopkv_decode_attention")
+
+
+def loopkv_auto_split(handle, batch, page_table_stride) -> int:
+    v = ctypes.c_int32()
+    _check(lib().loopkv_auto_split(handle, batch, page_table_stride, ctypes.byref(v)), "loopkv_auto_split")
+    return v.value
 
 
 def loopkv_get_cell_info(handle, layer, loop) -> CellInfo:
