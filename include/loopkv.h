@@ -244,6 +244,26 @@ loopkv_status loopkv_decode_attention(loopkv_plan plan, int32_t layer, int32_t l
                                       const loopkv_decode_opts* opts, float* out_dev,
                                       void* stream);
 
+/* loopkv_decode_attention for callers that cannot allocate device memory or must not touch
+ * the plan's arena workspace (code under HIP graph capture that owns no workspace, tight
+ * serving loops, harnesses that forbid allocation): identical arguments, semantics, results
+ * (bit for bit) and errors, except that the split partials and merge counters live in a fixed
+ * 4 MiB device array of the library, one per GPU, whose address is looked up (and whose
+ * counters are cleared) by loopkv_plan_load on that GPU. The call allocates nothing and
+ * issues only the decode launch. Limit: batch * num_kv_heads <= 16384 and
+ * batch * num_kv_heads * (number of splits) <= 7939 (the partials' 4 MiB - 64 KiB), else
+ * LOOPKV_ECAPACITY before anything is enqueued; shape.max_splits does not apply. The device
+ * current at the call must be the plan's (LOOPKV_EINVAL otherwise). Every call on a GPU shares
+ * that GPU's array: split calls that overlap in time on one GPU (two streams, two threads, two
+ * plans) race and give wrong results; the counters are back at zero after every call. */
+loopkv_status loopkv_decode_attention_static(loopkv_plan plan, int32_t layer, int32_t loop,
+                                             const void* q_dev, int32_t batch,
+                                             const int32_t* seq_lens_dev,
+                                             const int32_t* page_table_dev,
+                                             int32_t page_table_stride,
+                                             const loopkv_decode_opts* opts, float* out_dev,
+                                             void* stream);
+
 /* The split_tokens a decode with LOOPKV_SPLIT_AUTO uses for `batch` requests and a page table
  * of `page_table_stride` entries (context c = min(max_pages_per_seq, stride) * page_tokens):
  * 0 (no split) when batch * num_kv_heads rows already give every compute unit of the device

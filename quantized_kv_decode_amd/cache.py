@@ -63,8 +63,11 @@ class LoopKVCache:
                page_table: torch.Tensor, *, tau: float = 0.0, sm_scale: float = 0.0,
                split_tokens: int = 0, seed: torch.Tensor | None = None,
                fetch_mask: torch.Tensor | None = None, stats: torch.Tensor | None = None,
-               out: torch.Tensor | None = None, sink_seed: bool = True, stream=None) -> torch.Tensor:
-        """q: bf16 [B, H, D]; seq_lens: int32 [B] including the new token. Returns fp32 [B, H, D]."""
+               out: torch.Tensor | None = None, sink_seed: bool = True, stream=None,
+               static_workspace: bool = False) -> torch.Tensor:
+        """q: bf16 [B, H, D]; seq_lens: int32 [B] including the new token. Returns fp32 [B, H, D].
+        static_workspace: call loopkv_decode_attention_static (split workspace in the library's
+        fixed per-GPU array) instead of loopkv_decode_attention."""
         assert q.dtype == torch.bfloat16 and q.is_contiguous()
         B = q.shape[0]
         if out is None:
@@ -75,8 +78,9 @@ class LoopKVCache:
         if fetch_mask is not None:
             assert fetch_mask.dtype == torch.uint8 and fetch_mask.stride(2) == 1
             assert fetch_mask.stride(0) == fetch_mask.stride(1) * q.shape[1]
-        L.loopkv_decode_attention(self.handle, layer, loop, _ptr(q), B, _ptr(seq_lens), _ptr(page_table),
-                                  page_table.stride(0), opts, _ptr(out), _stream(stream))
+        fn = L.loopkv_decode_attention_static if static_workspace else L.loopkv_decode_attention
+        fn(self.handle, layer, loop, _ptr(q), B, _ptr(seq_lens), _ptr(page_table), page_table.stride(0),
+           opts, _ptr(out), _stream(stream))
         return out
 
     def auto_split(self, batch: int, page_table: torch.Tensor) -> int:

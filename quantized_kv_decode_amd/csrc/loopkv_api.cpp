@@ -307,6 +307,7 @@ loopkv_status loopkv_plan_load(const loopkv_shape* shape, const uint8_t* plan, v
     e = hipMemsetAsync(p->merge_dev, 0, (size_t)shape->max_batch * H * sizeof(int32_t), s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return LOOPKV_EHIP;
+  if (!static_workspace(p->device, s)) return LOOPKV_EHIP;
   *out = p.release();
   return LOOPKV_OK;
 } catch (const std::bad_alloc&) {
@@ -377,11 +378,15 @@ loopkv_status loopkv_quantize_append(loopkv_plan p, int32_t layer, int32_t loop,
   return e == hipSuccess ? LOOPKV_OK : LOOPKV_EHIP;
 }
 
-loopkv_status loopkv_decode_attention(loopkv_plan p, int32_t layer, int32_t loop,
-                                      const void* q, int32_t batch, const int32_t* seq_lens,
-                                      const int32_t* page_table, int32_t pt_stride,
-                                      const loopkv_decode_opts* opts, float* out,
-                                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points: `static_ws` takes the split partials and merge counters from the
+// per-device static array instead of the plan's arena.
+loopkv_status decode_impl(loopkv_plan p, int32_t layer, int32_t loop, const void* q, int32_t batch,
+                          const int32_t* seq_lens, const int32_t* page_table, int32_t pt_stride,
+                          const loopkv_decode_opts* opts, float* out, void* stream, bool static_ws) {
   if (!cell_ok(p, layer, loop)) return LOOPKV_EINVAL;
   if (!q || !seq_lens || !page_table || !out) return LOOPKV_EINVAL;
   if ((uintptr_t)q % 16 != 0) return LOOPKV_EINVAL;   // read in 16-byte pieces
@@ -393,12 +398,30 @@ loopkv_status loopkv_decode_attention(loopkv_plan p, int32_t layer, int32_t loop
   if (!std::isfinite(o.sm_scale) || o.sm_scale < 0.f) return LOOPKV_EINVAL;
   if (o.split_tokens != LOOPKV_SPLIT_AUTO && (o.split_tokens < 0 || o.split_tokens % kGroup != 0))
     return LOOPKV_EINVAL;
-  const Geom g = make_geom(p);
+  Geom g = make_geom(p);
   const int64_t ctx = decode_ctx(p, pt_stride);
   if (o.split_tokens == LOOPKV_SPLIT_AUTO) o.split_tokens = auto_split(p, batch, ctx);
   if (o.fetch_mask_dev && (int64_t)o.mask_stride < ctx) return LOOPKV_EINVAL;
   const int64_t n_split = o.split_tokens ? (ctx + o.split_tokens - 1) / o.split_tokens : 1;
-  if (n_split > p->shape.max_splits) return LOOPKV_ECAPACITY;
+  float* partials = p->partials_dev;
+  int32_t* counters = p->merge_dev;
+  if (static_ws) {
+    const uint64_t rows = (uint64_t)batch * g.H;
+    if (rows * sizeof(int32_t) > kStaticWsCounterBytes ||
+        rows * (uint64_t)n_split * (g.D + 2) * sizeof(float) > kStaticWsBytes - kStaticWsCounterBytes)
+      return LOOPKV_ECAPACITY;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != p->device) return LOOPKV_EINVAL;
+    // set up (address looked up, counters cleared) by loopkv_plan_load on this device, so this
+    // returns the kept address without a HIP call
+    void* ws = static_workspace(dev, static_cast<hipStream_t>(stream));
+    if (!ws) return LOOPKV_EHIP;
+    counters = static_cast<int32_t*>(ws);
+    partials = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kStaticWsCounterBytes);
+    g.max_splits = (int32_t)n_split;   // partial rows packed at this call's split count
+  } else if (n_split > p->shape.max_splits) {
+    return LOOPKV_ECAPACITY;
+  }
   const size_t i = (size_t)loop * p->shape.num_layers + layer;
   DecodeCall c;
   c.desc_dev = p->desc_dev + i;
@@ -416,12 +439,34 @@ loopkv_status loopkv_decode_attention(loopkv_plan p, int32_t layer, int32_t loop
   c.mask_stride = o.mask_stride;
   c.stats = o.stats_dev;
   c.out = out;
-  c.partials = p->partials_dev;
-  c.counters = p->merge_dev;
+  c.partials = partials;
+  c.counters = counters;
   c.order_by_len = 0;   // set by the launcher from the grid size
   c.sink_seed = o.no_sink_seed ? 0 : 1;
   hipError_t e = launch_decode(g, p->desc[i], c, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LOOPKV_OK : LOOPKV_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+loopkv_status loopkv_decode_attention(loopkv_plan p, int32_t layer, int32_t loop,
+                                      const void* q, int32_t batch, const int32_t* seq_lens,
+                                      const int32_t* page_table, int32_t pt_stride,
+                                      const loopkv_decode_opts* opts, float* out,
+                                      void* stream) {
+  return decode_impl(p, layer, loop, q, batch, seq_lens, page_table, pt_stride, opts, out, stream,
+                     false);
+}
+
+loopkv_status loopkv_decode_attention_static(loopkv_plan p, int32_t layer, int32_t loop,
+                                             const void* q, int32_t batch, const int32_t* seq_lens,
+                                             const int32_t* page_table, int32_t pt_stride,
+                                             const loopkv_decode_opts* opts, float* out,
+                                             void* stream) {
+  return decode_impl(p, layer, loop, q, batch, seq_lens, page_table, pt_stride, opts, out, stream,
+                     true);
 }
 
 }  // extern "C"

@@ -133,4 +133,13 @@ struct DecodeCall {
 hipError_t launch_decode(const Geom& g, const CellDesc& desc_host, const DecodeCall& c,
                          hipStream_t stream);
 
+// Fixed per-GPU workspace of loopkv_decode_attention_static (static_workspace.hip): merge
+// counters in the first kStaticWsCounterBytes, split partials after them.
+constexpr uint64_t kStaticWsBytes = 4ull << 20;          // 4 MiB per device
+constexpr uint64_t kStaticWsCounterBytes = 64ull << 10;  // counters for up to 16384 rows
+// Device address of the workspace on device `device`, which must be current. The first call
+// for a device looks the address up and clears the counters on `stream` (waiting for it);
+// later calls return the kept address without a HIP call. nullptr if a HIP call fails.
+void* static_workspace(int device, hipStream_t stream);
+
 }  // namespace loopkv

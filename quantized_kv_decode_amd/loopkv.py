@@ -70,6 +70,7 @@ class PlanCost(ctypes.Structure):
 SYMBOLS = ["loopkv_cache_bytes", "loopkv_plan_load", "loopkv_plan_free",
            "loopkv_quantize_append", "loopkv_decode_attention", "loopkv_get_cell_info",
            "loopkv_device_errors", "loopkv_plan_solve", "loopkv_auto_split",
+           "loopkv_decode_attention_static",
            "loopkv_status_string"]
 
 _lib = None
@@ -94,6 +95,7 @@ def lib() -> ctypes.CDLL:
         L.loopkv_plan_solve.argtypes = [ctypes.POINTER(Shape), vp, ctypes.POINTER(PlanBudget), vp,
                                         ctypes.POINTER(PlanCost)]
         L.loopkv_auto_split.argtypes = [vp, i32, i32, ctypes.POINTER(ctypes.c_int32)]
+        L.loopkv_decode_attention_static.argtypes = L.loopkv_decode_attention.argtypes
         L.loopkv_status_string.argtypes = [ctypes.c_int]
         L.loopkv_status_string.restype = ctypes.c_char_p
         for name in SYMBOLS:
@@ -155,6 +157,14 @@ def loopkv_decode_attention(handle, layer, loop, q_dev, batch, seq_lens_dev, pag
                                          page_table_dev, page_table_stride,
                                          ctypes.byref(opts) if opts is not None else None,
                                          out_dev, stream), "loopkv_decode_attention")
+
+
+def loopkv_decode_attention_static(handle, layer, loop, q_dev, batch, seq_lens_dev, page_table_dev,
+                                   page_table_stride, opts: DecodeOpts | None, out_dev, stream) -> None:
+    _check(lib().loopkv_decode_attention_static(handle, layer, loop, q_dev, batch, seq_lens_dev,
+                                                page_table_dev, page_table_stride,
+                                                ctypes.byref(opts) if opts is not None else None,
+                                                out_dev, stream), "loopkv_decode_attention_static")
 
 
 def loopkv_auto_split(handle, batch, page_table_stride) -> int:

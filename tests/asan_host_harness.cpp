@@ -12,6 +12,7 @@ namespace loopkv {
 hipError_t launch_append(const Geom&, const CellDesc*, const CellDesc&, const uint16_t*, const uint16_t*, int, int,
                          const int32_t*, const int32_t*, const int32_t*, int, hipStream_t) { return hipErrorUnknown; }
 hipError_t launch_decode(const Geom&, const CellDesc&, const DecodeCall&, hipStream_t) { return hipErrorUnknown; }
+void* static_workspace(int, hipStream_t) { return nullptr; }
 }
 int main() {
   std::mt19937_64 rng(7);
