@@ -266,11 +266,11 @@ loopkv_status loopkv_decode_attention_static(loopkv_plan plan, int32_t layer, in
 
 /* The split_tokens a decode with LOOPKV_SPLIT_AUTO uses for `batch` requests and a page table
  * of `page_table_stride` entries (context c = min(max_pages_per_seq, stride) * page_tokens):
- * 0 (no split) when batch * num_kv_heads rows already give every compute unit of the device
- * a workgroup or c <= 256; otherwise about one workgroup per compute unit as splits of at
- * least 256 tokens, at most 64 per row (section 3.4: up to 64 far blocks per decode row) and
- * at most shape.max_splits. Deterministic for a device, so a caller (or a test) can
- * reproduce the fetch mask. Host only. Errors: LOOPKV_EINVAL. */
+ * n = min(ceil(4 * CUs / (batch * num_kv_heads)), 64, shape.max_splits, floor(c / 2048)) splits
+ * (enough that the rows fill every compute unit of the device with four rows' waves, at most
+ * 64 far blocks per row as in section 3.4, none shorter than 2048 tokens); 0 (no split) when
+ * n <= 1, else ceil(c / n) rounded up to a multiple of 32. Deterministic for a device, so a
+ * caller (or a test) can reproduce the fetch mask. Host only. Errors: LOOPKV_EINVAL. */
 loopkv_status loopkv_auto_split(loopkv_plan plan, int32_t batch, int32_t page_table_stride,
                                 int32_t* split_tokens);
 

@@ -181,22 +181,23 @@ Geom make_geom(const loopkv_plan_s* p) {
   return g;
 }
 
-// The split used for split_tokens = LOOPKV_SPLIT_AUTO: none when the (request, head) rows
-// alone give every compute unit a workgroup; otherwise about kAutoWgPerCu workgroups per CU,
-// as runs of at least kAutoMinSplit tokens (one round of every wave of a row), at most 64 runs
-// per row (section 3.4: up to 64 far blocks per decode row) and at most max_splits.
-constexpr int64_t kAutoWgPerCu = 1;
-constexpr int64_t kAutoMinSplit = 256;
+// The split used for split_tokens = LOOPKV_SPLIT_AUTO. Enough splits that the (request, head)
+// rows fill every compute unit with a four-row workgroup (rows * splits >= 4 * CUs), but splits of
+// at least kAutoMinSplit tokens: a split restarts its running maximum at the seed, so short
+// splits fetch more low planes, and each split workgroup pays a fixed prologue and merge. At
+// most 64 splits per row (section 3.4: up to 64 far blocks per decode row) and max_splits.
+constexpr int64_t kAutoRowsPerCu = 4;
+constexpr int64_t kAutoMinSplit = 2048;
 
 int32_t auto_split(const loopkv_plan_s* p, int32_t batch, int64_t ctx) {
   const int64_t rows = (int64_t)batch * p->shape.num_kv_heads;
   const int64_t cus = std::max(p->cus, 1);
-  if (rows >= cus || ctx <= kAutoMinSplit) return 0;
-  int64_t n = (kAutoWgPerCu * cus + rows - 1) / rows;
+  int64_t n = (kAutoRowsPerCu * cus + rows - 1) / rows;
   n = std::min<int64_t>(n, std::min<int64_t>(64, p->shape.max_splits));
-  int64_t st = (ctx + n - 1) / n;
-  st = std::max<int64_t>((st + kGroup - 1) / kGroup * kGroup, kAutoMinSplit);
-  return (ctx + st - 1) / st > 1 ? (int32_t)st : 0;
+  n = std::min<int64_t>(n, ctx / kAutoMinSplit);
+  if (n <= 1) return 0;
+  const int64_t st = (ctx + n - 1) / n;
+  return (int32_t)((st + kGroup - 1) / kGroup * kGroup);
 }
 
 int64_t decode_ctx(const loopkv_plan_s* p, int32_t pt_stride) {

@@ -58,14 +58,13 @@ def test_decode_value_magnitudes(bits, scale):
 def _expected_auto_split(batch, heads, ctx, cus, max_splits):
     """The rule loopkv.h states for LOOPKV_SPLIT_AUTO."""
     rows = batch * heads
-    if rows >= cus or ctx <= 256:
+    n = min(-(-4 * cus // rows), 64, max_splits, ctx // 2048)
+    if n <= 1:
         return 0
-    n = min(-(-cus // rows), 64, max_splits)
-    st = max(-(-(-(-ctx // n)) // 32) * 32, 256)
-    return st if -(-ctx // st) > 1 else 0
+    return -(-(-(-ctx // n)) // 32) * 32
 
 
-@pytest.mark.parametrize("batch,n", [(1, 8192), (2, 3000), (40, 1000)])
+@pytest.mark.parametrize("batch,n", [(1, 8192), (3, 6000), (40, 1000)])
 def test_decode_auto_split(batch, n):
     """A decode with split_tokens = LOOPKV_SPLIT_AUTO equals the oracle at the split that
     loopkv_auto_split reports, for a plan with 4-bit, 2-bit and reusing cells; the reported split
