@@ -336,9 +336,13 @@ def decode_head(q, qh: QuantHead | None, tail_k, tail_v, *, sm_scale, tau, m0=-m
 #
 #   KSZ  4*D bytes      fp16 (s, z) per channel for the key group that starts in this page
 #                       (unused in a page that does not start a group)
-#   KC   P*D*b/8 bytes  key codes, 32-bit words W[cb][t] at word cb*P + t:
-#                       INT4: channel 8*cb + i in bits 4i..4i+3 (cb < D/8)
-#                       INT2: channel 16*cb + i in bits 2i..2i+1 (cb < D/16)
+#   KC   P*D*b/8 bytes  key codes, token-major 32-bit words W[t][w] at word t*(D*b/32) + w:
+#                       INT4: word w holds channels 8w..8w+7; channel 8w + i (i < 4) in bits
+#                             8i..8i+3 and channel 8w + 4 + i in bits 8i+4..8i+7
+#                       INT2: word w holds channels 16w..16w+15; channel 16w + 4k + i
+#                             (k, i < 4) in bits 8i+2k..8i+2k+1
+#                       (masking a word's nibbles -- or 2-bit fields -- into bytes leaves four
+#                       consecutive channels in each 32-bit register)
 #   VC   P*D/4 bytes    INT4 high plane, or INT2 value codes: W[cb][t] at word cb*P + t,
 #                       channel 16*cb + i in bits 2i..2i+1
 #   VSZ  4*P*NVG bytes  fp16 (s, z) per (token, value group), token-major
@@ -371,6 +375,32 @@ def _pack_words_colmajor(codes, per_word, width):
     shifts = (np.arange(per_word, dtype=np.uint64) * width)
     words = (c << shifts).sum(axis=2).astype(np.uint32)       # [P, D/per_word]
     return words.T.copy()                                     # [cb, t]
+
+
+def _kc_field_channels(bits):
+    """Channel (within its word) held by each field of a key-code word, low field first."""
+    if bits == INT4:
+        return np.array([(f % 2) * 4 + f // 2 for f in range(8)])
+    return np.array([4 * (f % 4) + f // 4 for f in range(16)])
+
+
+def _pack_kc(codes, bits):
+    """Key codes [P, D] -> token-major uint32 words [P, D*bits/32] (the KC field order above)."""
+    p, d = codes.shape
+    per_word = 32 // bits
+    ch = _kc_field_channels(bits)
+    c = codes.astype(np.uint64).reshape(p, d // per_word, per_word)[:, :, ch]   # field order
+    shifts = np.arange(per_word, dtype=np.uint64) * bits
+    return (c << shifts).sum(axis=2).astype(np.uint32)
+
+
+def _unpack_kc(words, bits):
+    """Inverse of _pack_kc: uint32 [P, D*bits/32] -> codes [P, D]."""
+    per_word = 32 // bits
+    fields = _unpack_words(words, per_word, bits).reshape(words.shape[0], -1, per_word)
+    out = np.empty_like(fields)
+    out[:, :, _kc_field_channels(bits)] = fields
+    return out.reshape(words.shape[0], -1)
 
 
 def _unpack_words(words, per_word, width):
@@ -408,12 +438,12 @@ def pack_head_block(bits, page_tokens, k_codes, v_codes, v_s, v_z, k_s=None, k_z
     if k_s is not None:
         put("ksz", _fp16_pairs(k_s, k_z))
     if bits == INT4:
-        put("kc", _pack_words_colmajor(k_codes, 8, 4))
+        put("kc", _pack_kc(k_codes, INT4))
         hi, lo = split_planes(v_codes)
         put("vc", _pack_words_colmajor(hi, 16, 2))
         put("vlo", _pack_words_colmajor(lo, 16, 2).T.copy())   # token-major
     else:
-        put("kc", _pack_words_colmajor(k_codes, 16, 2))
+        put("kc", _pack_kc(k_codes, INT2))
         put("vc", _pack_words_colmajor(v_codes, 16, 2))
     put("vsz", _fp16_pairs(v_s, v_z))
     return buf
@@ -433,14 +463,12 @@ def unpack_head_block(bits, page_tokens, buf, d=128, v_group=128):
     nvg = d // v_group
     vsz = get("vsz", np.uint16).reshape(p, nvg, 2).view(np.float16).astype(np.float64)
     if bits == INT4:
-        kw = get("kc", np.uint32).reshape(d // 8, p).T          # [t, cb]
-        k_codes = _unpack_words(kw, 8, 4)
+        k_codes = _unpack_kc(get("kc", np.uint32).reshape(p, d // 8), INT4)
         hw = get("vc", np.uint32).reshape(d // 16, p).T
         lw = get("vlo", np.uint32).reshape(p, d // 16)
         v_codes = 4 * _unpack_words(hw, 16, 2) + _unpack_words(lw, 16, 2)
     else:
-        kw = get("kc", np.uint32).reshape(d // 16, p).T
-        k_codes = _unpack_words(kw, 16, 2)
+        k_codes = _unpack_kc(get("kc", np.uint32).reshape(p, d // 16), INT2)
         vw = get("vc", np.uint32).reshape(d // 16, p).T
         v_codes = _unpack_words(vw, 16, 2)
     return dict(k_codes=k_codes, v_codes=v_codes, k_s=ksz[:, 0], k_z=ksz[:, 1],

@@ -265,16 +265,23 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
   }
   __syncthreads();
 
-  // Key code words W[cb][t]: KPW channels of one token per word.
+  // Key code words, token-major W[t][w]: KPW channels of one token per word, in the field order
+  // that masking a word into bytes turns into four consecutive channels per 32-bit register
+  // (INT4: channel 8w + i in bits 8i..8i+3, 8w + 4 + i in bits 8i+4..8i+7; INT2: channel
+  // 16w + 4k + i in bits 8i+2k..8i+2k+1).
   constexpr int KPW = 32 / BITS;
-  for (int w = tid; w < (kHeadDim / KPW) * kGroup; w += 128) {
-    const int cb = w / kGroup, tt = w % kGroup;
+  constexpr int NKW = kHeadDim / KPW;   // words per token
+  for (int w = tid; w < NKW * kGroup; w += 128) {
+    const int tt = w / NKW, cw = w % NKW;
     uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) word |= (uint32_t)kcode[tt][cb * KPW + i] << (BITS * i);
+    for (int f = 0; f < KPW; ++f) {
+      const int ch = BITS == 4 ? (f % 2) * 4 + f / 2 : 4 * (f % 4) + f / 4;
+      word |= (uint32_t)kcode[tt][cw * KPW + ch] << (BITS * f);
+    }
     int tl;
     uint8_t* blk = tok_block(tt, &tl);
-    reinterpret_cast<uint32_t*>(blk + lay.kc)[cb * g.P + tl] = word;
+    reinterpret_cast<uint32_t*>(blk + lay.kc)[tl * NKW + cw] = word;
   }
 }
 

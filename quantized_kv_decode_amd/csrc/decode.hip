@@ -28,11 +28,18 @@
 // the next, before that round's barrier, where a wave would otherwise wait for the others.
 //
 // Arithmetic:
-//  - keys: a 4-bit code in the low bits of an fp8 (E4M3) byte converts exactly to code * u
-//    (u = the value of byte 0x01), since E4M3's subnormals and first binade are evenly spaced
-//    up to 15u; a 2-bit code in the low bits of an fp4 (E2M1) nibble converts exactly to
-//    code / 2. One conversion gives two codes as floats. The score is an fp32 FMA chain, so
-//    the hot/cold test sees fp32-accurate scores.
+//  - keys: the scores of a round's 64 tokens are four block-scaled fp8 MFMAs (16 tokens x 128
+//    channels each, v_mfma_scale_f32_16x16x128_f8f6f4). Operand B is the key codes: a 4-bit
+//    or 2-bit code in the low bits of an fp8 (E4M3) byte is exactly code * 2^-9 (E4M3's
+//    subnormals and first binade are evenly spaced up to 15 * 2^-9), so masking the stored
+//    words into bytes is the whole conversion. Operand A is q * s_K (the key scale folded
+//    into the query, per group and channel) written as a 24-bit integer relative to the
+//    largest magnitude of its 32-channel scale block, offset by 2^23 and split into six
+//    base-16 digits (rows of fp8 integers 0..15), plus a constant row that removes the offset;
+//    each row and block carries its power of two in the MFMA's E8M0 block scale. Every product and block
+//    sum is exact, so the score keeps fp32 accuracy (22 bits of q * s_K per block) and the
+//    hot/cold test sees fp32-accurate scores. The key zero point enters as the accumulator's
+//    initial value (sum over channels of q * z_K).
 //  - values (INT4 high plane, INT2 codes): two tokens' words are interleaved with one byte
 //    permute so each 16-bit half holds one token's channels; a code moved to mantissa bits 4..9
 //    and OR-ed with the exponent of 1.0 is the fp16 number 1 + c/64, 1 + c/16 or 1 + c/4, and one
@@ -59,6 +66,8 @@ constexpr float kWExact = 256.f;         // 2^8: largest K while exact tokens ar
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef const LKV_GLOBAL uint8_t* gbytes;
 
 template <class T>
@@ -146,33 +155,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Byte SEL of w as two fp4 (E2M1) numbers, low nibble first, times 2. A 2-bit code in the low
-// bits of a nibble (sign and high exponent bit clear) is the E2M1 number code / 2: 0, 0.5
-// (the subnormal), 1, 1.5.
-template <int SEL>
-__device__ __forceinline__ float2v fp4x2(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 2.0f, SEL);
-}
-
-// 16 two-bit codes of a word (channel i at bits 2i) as floats equal to the codes.
-__device__ __forceinline__ void unpack16(uint32_t w, float (&x)[16]) {
-  const uint32_t e = w & 0x33333333u;          // nibble j: code of channel 2j
-  const uint32_t o = (w >> 2) & 0x33333333u;   // nibble j: code of channel 2j + 1
-  const float2v e0 = fp4x2<0>(e), e1 = fp4x2<1>(e), e2 = fp4x2<2>(e), e3 = fp4x2<3>(e);
-  const float2v o0 = fp4x2<0>(o), o1 = fp4x2<1>(o), o2 = fp4x2<2>(o), o3 = fp4x2<3>(o);
-  x[0] = e0.x; x[2] = e0.y; x[4] = e1.x; x[6] = e1.y; x[8] = e2.x; x[10] = e2.y; x[12] = e3.x; x[14] = e3.y;
-  x[1] = o0.x; x[3] = o0.y; x[5] = o1.x; x[7] = o1.y; x[9] = o2.x; x[11] = o2.y; x[13] = o3.x; x[15] = o3.y;
-}
-
-// 8 four-bit codes of a word (channel i at bits 4i) as floats: code * u.
-__device__ __forceinline__ void unpack8(uint32_t w, float (&x)[8]) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  float2v a = cvt2<false>(lo), b = cvt2<true>(lo);   // 0,2 | 4,6
-  float2v c = cvt2<false>(hi), d = cvt2<true>(hi);   // 1,3 | 5,7
-  x[0] = a.x; x[2] = a.y; x[4] = b.x; x[6] = b.y;
-  x[1] = c.x; x[3] = c.y; x[5] = d.x; x[7] = d.y;
-}
-
 // (x & m) | o in one VALU op. VOP3 takes no literal constant and at most one SGPR on gfx950,
 // so the mask is held in a VGPR and the OR constant in an SGPR (Masks below).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
@@ -213,8 +195,10 @@ __device__ __forceinline__ void dot2_pair(uint32_t w0, uint32_t w1, half2v wp, c
 template <int NVG, int NW>
 struct Smem {
   alignas(16) float q[kHeadDim];
-  alignas(16) float qv[kHeadDim];         // q / u, odd INT2 channels / (4u): the key operand
-  alignas(16) float red[NW][2][16][36];   // per-wave key partials [half][channel block][token]
+  // Score-MFMA operand A per wave: [group of the pair][32-channel block][row][32 channels].
+  // Rows 0..5 (the pair's first group) and 8..13 (its second) hold the base-16 digits of
+  // q * s_K, rows 6 and 14 the constant -1 of the digits' offset, the others stay zero.
+  alignas(16) uint8_t akey[NW][2][4][16][32];
   // Per-wave value weights [round parity][wave][value group][token of pair] and hot tokens
   // (token of pair, page id); the low planes of a round are added in the next one, which reads
   // that round's copies.
@@ -236,10 +220,9 @@ struct Smem {
 // after this round's last use of it, so one set of registers keeps a round of loads in flight.
 template <int BITS, int NVG>
 struct PairRegs {
-  static constexpr int KCW = BITS == 4 ? 4 : 2;   // 16-byte loads of key code words
-  static constexpr int KSW = BITS == 4 ? 2 : 4;   // 16-byte loads of key (s, z) words
-  u32x4 kc[KCW];
-  u32x4 ksz[KSW];
+  static constexpr int KCT = BITS == 4 ? 4 : 2;   // key-code words per lane and tile
+  uint32_t kc[4][KCT];   // 32 channels of one token of each 16-token tile
+  u32x4 ksz;             // (s, z) of the lane's four channels 4u..4u+3 in its group
   u32x4 vc[2];
   uint32_t vsz[NVG];
 };
@@ -252,27 +235,29 @@ struct RowCtx {
   uint32_t* err;
 };
 
-// Page ids a lane needs for one pair of groups: the page holding its token (lanes 0..31 take
-// the pair's first group, lanes 32..63 the second) and, with 16-token pages, the group's first
-// page, which holds the key scales. They are loaded a round before the pair's data.
-struct LaneIds {
-  int tok, first;
-};
-
+// Page ids of one round's pair of groups: with PPG pages per 32-token group, entry j < 2*PPG is
+// the page of group (first group of the pair + j / PPG), page j % PPG of it. Lane j % (2*PPG)
+// loads entry j, a round before the pair's data; the ids are then read back wave-uniform.
 template <int P>
-__device__ __forceinline__ LaneIds load_ids(const RowCtx& r, int g, int ge, int lane) {
-  constexpr int PPG = kGroup / P;   // pages per group
-  const int gg = min(g + (lane >> 5), ge - 1);   // never past the history
-  LaneIds id;
-  id.tok = r.pt_row[gg * PPG + (PPG == 2 ? ((lane >> 4) & 1) : 0)];
-  id.first = PPG == 2 ? r.pt_row[gg * PPG] : id.tok;
-  return id;
+__device__ __forceinline__ int load_pair_ids(const RowCtx& r, int g, int ge, int lane) {
+  constexpr int PPG = kGroup / P;
+  const int j = lane & (2 * PPG - 1);
+  const int gg = min(g + j / PPG, ge - 1);   // never past the history
+  return r.pt_row[gg * PPG + j % PPG];
 }
 
 // A page id outside the pool is reported and replaced by page 0.
 __device__ __forceinline__ int checked_page(const RowCtx& r, int pid) {
   if ((uint32_t)pid >= r.num_pages) {
     atomicOr(r.err, (uint32_t)kErrPage);
+    pid = 0;
+  }
+  return pid;
+}
+// The same for a wave-uniform id: one lane reports.
+__device__ __forceinline__ int checked_page_u(const RowCtx& r, int pid, int lane) {
+  if ((uint32_t)pid >= r.num_pages) {
+    if (lane == 0) atomicOr(r.err, (uint32_t)kErrPage);
     pid = 0;
   }
   return pid;
@@ -293,43 +278,66 @@ struct LaneOffs {
 
 template <int BITS, int NVG, int P>
 __device__ __forceinline__ LaneOffs lane_offsets(const Layout& lay, int lane) {
-  constexpr int KCH = 32 / BITS;
-  constexpr int NCB = kHeadDim / KCH;
-  constexpr int KTOK = NCB;                 // tokens per lane in a 32-lane half
   const int hl = lane & 31;
-  const int cb = hl % NCB, t0 = (hl / NCB) * KTOK;
   const int cbv = hl & 7, tv = (hl >> 3) * 8;
   LaneOffs o;
-  o.kc = lay.kc + 4 * (cb * P + t0 % P);         // key codes of KTOK tokens of block cb
-  o.ksz = lay.ksz + 4 * cb * KCH;                // key (s, z) of the lane's channels
+  // key codes: token lane % 16 of a tile, channels 32 * (lane / 16) .. + 31 (token-major rows)
+  o.kc = lay.kc + (lane & 15) * (kHeadDim * BITS / 8) + (lane >> 4) * (32 * BITS / 8);
+  o.ksz = lay.ksz + 16 * hl;                     // key (s, z) of channels 4hl .. 4hl + 3
   o.vc = lay.vc + 4 * (cbv * P + tv % P);        // value codes / high plane: 16 ch x 8 tokens
   o.vsz = lay.vsz + 4 * (hl % P) * NVG;          // value (s, z) of token hl
   return o;
 }
 
-// Page addresses of a lane's loads for one pair of groups.
+// Page addresses of one pair of groups: the page of each 16-token key tile and the page of the
+// lane's group's key scales (wave-uniform within each half), and the page of the lane's token.
 struct PairPages {
-  gbytes tok, first;
+  gbytes kt[4];
+  gbytes ksz;
+  gbytes tok;
   int tok_pid;
 };
 
 template <int P>
-__device__ __forceinline__ PairPages pair_pages(const RowCtx& r, const LaneIds& id) {
+__device__ __forceinline__ PairPages pair_pages(const RowCtx& r, int idv, int lane) {
+  constexpr int PPG = kGroup / P;
+  int pid[2 * PPG];
+  gbytes pg[2 * PPG];
+#pragma unroll
+  for (int j = 0; j < 2 * PPG; ++j) {
+    pid[j] = checked_page_u(r, __builtin_amdgcn_readlane(idv, j), lane);
+    pg[j] = r.pool + (uint64_t)(uint32_t)pid[j] * r.page_bytes;
+  }
   PairPages pp;
-  pp.tok_pid = checked_page(r, id.tok);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pp.kt[k] = pg[PPG == 1 ? k / 2 : k];
+  const bool second = lane >= 32;
+  pp.ksz = second ? pg[PPG] : pg[0];
+  if (PPG == 1) {
+    pp.tok_pid = second ? pid[1] : pid[0];
+  } else {
+    const bool hi16 = (lane & 16) != 0;
+    pp.tok_pid = second ? (hi16 ? pid[3] : pid[2]) : (hi16 ? pid[1] : pid[0]);
+  }
   pp.tok = page_at(r, pp.tok_pid);
-  pp.first = P == kGroup ? pp.tok : page_at(r, checked_page(r, id.first));
   return pp;
 }
 
-template <int BITS, int NVG>
-__device__ __forceinline__ void load_keys(PairRegs<BITS, NVG>& g, const PairPages& pp, const LaneOffs& o) {
-  const LKV_GLOBAL u32x4* kc = gp<u32x4>(pp.tok + o.kc);
+template <int BITS, int P, int NVG>
+__device__ __forceinline__ void load_kc(PairRegs<BITS, NVG>& g, const PairPages& pp, const LaneOffs& o) {
+  constexpr int ROW = kHeadDim * BITS / 8;   // bytes of one token's key codes
 #pragma unroll
-  for (int i = 0; i < PairRegs<BITS, NVG>::KCW; ++i) g.kc[i] = kc[i];
-  const LKV_GLOBAL u32x4* ksz = gp<u32x4>(pp.first + o.ksz);
-#pragma unroll
-  for (int i = 0; i < PairRegs<BITS, NVG>::KSW; ++i) g.ksz[i] = ksz[i];
+  for (int k = 0; k < 4; ++k) {
+    // with 32-token pages the second tile of a group is 16 rows further in the same page
+    const gbytes a = pp.kt[k] + o.kc + (P == kGroup && (k & 1) ? 16 * ROW : 0);
+    if (BITS == 4) {
+      const u32x4 v = *gp<u32x4>(a);
+      g.kc[k][0] = v.x; g.kc[k][1] = v.y; g.kc[k][2] = v.z; g.kc[k][3] = v.w;
+    } else {
+      const uint64_t v = *gp<uint64_t>(a);
+      g.kc[k][0] = (uint32_t)v; g.kc[k][1] = (uint32_t)(v >> 32);
+    }
+  }
 }
 template <int BITS, int NVG>
 __device__ __forceinline__ void load_vsz(PairRegs<BITS, NVG>& g, const PairPages& pp, const LaneOffs& o) {
@@ -369,12 +377,63 @@ __device__ __forceinline__ void scale_values(WaveState<NVG>& st, float r) {
 }
 
 struct RoundConst {
-  float scale2, log2tau, u;
+  float scale2, log2tau;
   bool gated;
   int w, lane, gs, ge;
   uint8_t* mask_row;
   Masks mk;
 };
+
+// Score-MFMA constants of a lane: scale offsets of A row lane % 16 in each group of the pair
+// (-1: a zero row), and the byte addresses of lanes holding the exponent of block lane / 16 in
+// the pair's first and second group. A row r: digit rows 0..5 / 8..13 scale by 2^(4m + E - 13)
+// (E8M0 byte 4m + E + 114), offset rows 6 / 14 by 2^(E + 1).
+struct KeyLaneConst {
+  int sofs0, sofs1, eaddr0, eaddr1;
+};
+__device__ __forceinline__ KeyLaneConst key_lane_const(int lane) {
+  KeyLaneConst c;
+  const int ar = lane & 15;
+  c.sofs0 = ar <= 5 ? 114 + 4 * ar : ar == 6 ? 128 : -1;
+  c.sofs1 = ar >= 8 && ar <= 13 ? 114 + 4 * (ar - 8) : ar == 14 ? 128 : -1;
+  const int q = lane >> 4;
+  const int src = q == 0 ? 0 : q == 1 ? 16 : q == 2 ? 4 : 20;
+  c.eaddr0 = 4 * src;          // a lane whose channels fall in block lane / 16, first group
+  c.eaddr1 = 4 * (32 + src);   // and second group
+  return c;
+}
+
+constexpr int kCodeScale = 127 + 9;   // E8M0 2^9: a code c in an fp8 byte is c * 2^-9
+
+// Key codes of one 16-token tile (32 channels of one token per lane) as fp8 bytes: four
+// consecutive channels per register (the stored field order makes the masks enough).
+template <int BITS>
+__device__ __forceinline__ v8i spread_codes(const uint32_t (&w)[BITS == 4 ? 4 : 2]) {
+  v8i b;
+  if (BITS == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b[2 * j] = (int)(w[j] & 0x0F0F0F0Fu);
+      b[2 * j + 1] = (int)((w[j] >> 4) & 0x0F0F0F0Fu);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) b[4 * j + k] = (int)((w[j] >> (2 * k)) & 0x03030303u);
+  }
+  return b;
+}
+
+__device__ __forceinline__ v4f mfma_keys(const v8i& a, const v8i& b, const v4f& c, int scale_a) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, kCodeScale);
+}
+
+// Sum of a float over lanes l and l ^ 16 (rows 0+1 and 2+3 of the wave).
+__device__ __forceinline__ float add_swap16(float v) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
 
 // Adds the low planes loaded in the previous round (parity pr), before this round changes the
 // wave's maximum, so that round's weights still apply. Pass j covers hot tokens 16j .. 16j+15:
@@ -400,15 +459,16 @@ __device__ __forceinline__ void add_prev_lo(Smem<NVG, NW>& sm, WaveState<NVG>& s
 
 template <int BITS, int NVG, int P, int NW>
 __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st,
-                                           PairRegs<BITS, NVG>& cur, int& pid_cur, LaneIds& nid,
-                                           const RowCtx& r, const LaneOffs& lo, const RoundConst& k,
-                                           int rd) {
-  constexpr int KCH = 32 / BITS;
-  constexpr int NCB = kHeadDim / KCH;
-  constexpr int KTOK = NCB;
-  const int w = k.w, lane = k.lane;
+                                           PairRegs<BITS, NVG>& cur, int& pid_cur, int& nid,
+                                           const RowCtx& r, const RoundConst& k, int rd) {
+  const int w = k.w;
+  // The lane index, opaque to the compiler: values derived from it are formed again in every
+  // round instead of being kept live (in registers, or spilled) across the loop.
+  int lane = k.lane;
+  asm volatile("" : "+v"(lane));
+  constexpr Layout lay_r = head_layout(BITS, P, kHeadDim, NVG);
+  const LaneOffs lo = lane_offsets<BITS, NVG, P>(lay_r, lane);
   const int half = lane >> 5, hl = lane & 31;
-  const int cb = hl % NCB, t0 = (hl / NCB) * KTOK;
   const int cbv = lane & 7;
   const int vg_lane = (cbv * 16) / (kHeadDim / NVG);
   const int gA = k.gs + rd * 2 * NW + 2 * w;
@@ -419,61 +479,92 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   // issued on every round, also when the wave has no next pair (then it re-reads the split's
   // last group, which is cached): with a fixed number of loads per round every wait leaves
   // the younger loads in flight.
-  const PairPages np = pair_pages<P>(r, nid);
-  nid = load_ids<P>(r, gA + 4 * NW, k.ge, lane);
-
-  float qv[KCH];   // the lane's key operand (q / u), re-read from LDS to spare registers
-  {
-    const float4* qp = reinterpret_cast<const float4*>(&sm.qv[cb * KCH]);
-#pragma unroll
-    for (int i = 0; i < KCH / 4; ++i) {
-      const float4 v = qp[i];
-      qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
-    }
-  }
+  const PairPages np = pair_pages<P>(r, nid, lane);
+  nid = load_pair_ids<P>(r, gA + 4 * NW, k.ge, lane);
 
   // ---- scores of both groups (key codes read first, section 3.3)
   // Every step below runs also on a wave without groups this round (its scores are -inf and
   // its weights 0): then every path through the round consumes the same loads.
   float s2;
   {
-    float qs[KCH], ke = 0.f;
-    const uint32_t* kszw = reinterpret_cast<const uint32_t*>(cur.ksz);
+    // Operand A: lane (half, hl) holds channels 4hl .. 4hl+3 of group `half` of the pair;
+    // q * s_K (the key scale folded into the query, Appendix "History reader") and q * z_K.
+    const float4 qf = *reinterpret_cast<const float4*>(&sm.q[4 * hl]);
+    const float qv[4] = {qf.x, qf.y, qf.z, qf.w};
+    const uint32_t szw[4] = {cur.ksz.x, cur.ksz.y, cur.ksz.z, cur.ksz.w};
+    float qs[4], ke = 0.f, am = 0.f;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const uint32_t sz = kszw[i];
-      qs[i] = fmaf(qv[i], f16_lo(sz), 0.f);      // fp16 operand: one v_fma_mix_f32
-      ke = fmaf(qv[i], f16_hi(sz), ke);
+    for (int i = 0; i < 4; ++i) {
+      qs[i] = fmaf(qv[i], f16_lo(szw[i]), 0.f);   // fp16 operand: one v_fma_mix_f32
+      ke = fmaf(qv[i], f16_hi(szw[i]), ke);
+      am = dmax(am, fabsf(qs[i]));
     }
-    // kappa = sum_c q_c * z_c (the INT4 operand carries 1/u)
-    const float kappa = BITS == 4 ? ke * k.u : ke;
-    const uint32_t* kw = reinterpret_cast<const uint32_t*>(cur.kc);
-    float part[KTOK];
+    cur.ksz = *gp<u32x4>(np.ksz + lo.ksz);   // next round's key scales
+    // kappa = sum over the group's 128 channels of q * z_K: the 32 lanes of the half
+    ke = add_swap16(row_sum16(ke));
+    // The MFMA scales A row r by one E8M0 value per 32 channels, from lane r + 16 * b of its
+    // scale operand for block b: b = 0 takes channels 0..15 and 32..47, b = 1 64..79 and
+    // 96..111, b = 2 16..31 and 48..63, b = 3 80..95 and 112..127 (bytes 0..15 or 16..31 of
+    // the lanes holding channels 0..63 or 64..127). Here the largest |q * s_K| of the lane's
+    // block (8 lanes: quads 0 and 2, or 1 and 3, of its 16-lane row): |q * s_K| < 2^E.
+    am = dmax(am, dpp_mov<0xB1>(am));
+    am = dmax(am, dpp_mov<0x4E>(am));
+    am = dmax(am, dpp_mov<0x128>(am));
+    const int E = __builtin_amdgcn_frexp_expf(am);
+    const float sc = __builtin_ldexpf(1.f, 22 - E);
+    // 2^23 + q * s_K * 2^(22 - E), rounded: 24 bits, six base-16 digits
+    uint32_t X[4];
 #pragma unroll
-    for (int j = 0; j < KTOK; ++j) {
-      float a = kappa;
-      if (BITS == 4) {
-        float x[8];
-        unpack8(kw[j], x);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a = fmaf(qs[i], x[i], a);
-      } else {
-        float x[16];
-        unpack16(kw[j], x);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) a = fmaf(qs[i], x[i], a);
-      }
-      part[j] = a;
-    }
-    float* red = &sm.red[w][half][cb][t0];
-#pragma unroll
-    for (int j = 0; j < KTOK; j += 4)
-      *reinterpret_cast<float4*>(red + j) = make_float4(part[j], part[j + 1], part[j + 2], part[j + 3]);
-    load_keys<BITS, NVG>(cur, np, lo);   // next round's keys
+    for (int i = 0; i < 4; ++i) X[i] = (uint32_t)fmaf(qs[i], sc, 8388608.5f);
+    const uint32_t a01 = __builtin_amdgcn_perm(X[1], X[0], 0x05010400u);   // X0.b0 X1.b0 X0.b1 X1.b1
+    const uint32_t a23 = __builtin_amdgcn_perm(X[3], X[2], 0x05010400u);
+    const uint32_t l01 = a01 & 0x0F0F0F0Fu, h01 = (a01 >> 4) & 0x0F0F0F0Fu;
+    const uint32_t l23 = a23 & 0x0F0F0F0Fu, h23 = (a23 >> 4) & 0x0F0F0F0Fu;
+    const uint32_t c01 = __builtin_amdgcn_perm(X[1], X[0], 0x05010602u);   // X0.b2 X1.b2 ..
+    const uint32_t c23 = __builtin_amdgcn_perm(X[3], X[2], 0x05010602u);
+    const uint32_t cc = __builtin_amdgcn_perm(c23, c01, 0x05040100u);      // X0.b2 X1.b2 X2.b2 X3.b2
+    // digit m of the four channels, one byte each, into row (8 * half + m) of the block's A
+    uint8_t* arow = &sm.akey[w][half][hl >> 3][half * 8][4 * (hl & 7)];
+    *reinterpret_cast<uint32_t*>(arow + 0 * 32) = __builtin_amdgcn_perm(l23, l01, 0x05040100u);
+    *reinterpret_cast<uint32_t*>(arow + 1 * 32) = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
+    *reinterpret_cast<uint32_t*>(arow + 2 * 32) = __builtin_amdgcn_perm(l23, l01, 0x07060302u);
+    *reinterpret_cast<uint32_t*>(arow + 3 * 32) = __builtin_amdgcn_perm(h23, h01, 0x07060302u);
+    *reinterpret_cast<uint32_t*>(arow + 4 * 32) = cc & 0x0F0F0F0Fu;
+    *reinterpret_cast<uint32_t*>(arow + 5 * 32) = (cc >> 4) & 0x0F0F0F0Fu;
+    // scale of A row r = lane % 16, block lane / 16: digit m carries 2^(4m + E - 22), the
+    // offset row -2^(E + 1), times the fp8 units 2^9 of a digit byte; E of that block comes
+    // from a lane of the block in each half
+    const KeyLaneConst kl = key_lane_const(lane);
+    const int eA = __builtin_amdgcn_ds_bpermute(kl.eaddr0, E);
+    const int eB = __builtin_amdgcn_ds_bpermute(kl.eaddr1, E);
+    const int scA = kl.sofs0 < 0 ? 127 : min(max(eA + kl.sofs0, 0), 254);
+    const int scB = kl.sofs1 < 0 ? 127 : min(max(eB + kl.sofs1, 0), 254);
     wave_lds_sync();
-    float raw = 0.f;
+    // Operand B: the codes of tiles 0, 1 (first group) and 2, 3 (second group). D rows 0..7 take
+    // the first group (lanes 0..31), rows 8..15 the second (lanes 32..63); both accumulators
+    // start at kappa in row 0 / row 8. One A and one B operand are live at a time.
+    const v4f c0 = {(lane & 16) ? 0.f : ke, 0.f, 0.f, 0.f};
+    // tiles 0 and 2 (the first 16 tokens of each group), then tiles 1 and 3: one accumulator,
+    // one A and one B operand live at a time; A is read again from LDS for the second pair
+    float z[2];
 #pragma unroll
-    for (int kk = 0; kk < NCB; ++kk) raw += sm.red[w][half][kk][hl];
+    for (int t = 0; t < 2; ++t) {
+      v4f d;
+      {
+        const v8i A0 = *reinterpret_cast<const v8i*>(&sm.akey[w][0][lane >> 4][lane & 15][0]);
+        d = mfma_keys(A0, spread_codes<BITS>(cur.kc[t]), c0, scA);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const v8i A1 = *reinterpret_cast<const v8i*>(&sm.akey[w][1][lane >> 4][lane & 15][0]);
+        d = mfma_keys(A1, spread_codes<BITS>(cur.kc[2 + t]), d, scB);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // token t of a tile: rows in lanes t, t + 16 (first group) or t + 32, t + 48 (second)
+      z[t] = add_swap16(d[0] + d[1] + d[2] + d[3]);
+    }
+    load_kc<BITS, P, NVG>(cur, np, lo);   // next round's key codes
+    const float raw = (lane & 16) ? z[1] : z[0];   // lane = token of the pair, as below
     s2 = my_valid ? raw * k.scale2 : -INFINITY;
   }
   const float rm = row_max16(s2);
@@ -818,18 +909,23 @@ void decode_kernel(DecodeParams prm) {
     __syncthreads();
     b = s_b;
   }
-  const float u = cvt2<false>(1u).x;            // value of fp8 byte 0x01
-  const float inv_u = 1.0f / u;
-
   if (tid < kHeadDim) {
     const uint16_t qb = c.q[((size_t)b * H + h) * kHeadDim + tid];
-    const float q = __uint_as_float((uint32_t)qb << 16);
-    sm.q[tid] = q;
-    // key operand: q itself for INT2 codes (converted to their values), q / u for INT4 codes
-    // (converted to code * u)
-    sm.qv[tid] = BITS == 2 ? q : q * inv_u;
+    sm.q[tid] = __uint_as_float((uint32_t)qb << 16);
   }
   if (tid == 0) sm.cnt_hot = 0;
+  {
+    // The wave's score-MFMA operand A: zero rows, and the constant -1 (fp8 0xB8) in the offset
+    // rows 6 (first group of a pair) and 14 (second); the digit rows are rewritten every round.
+    uint8_t* ak = &sm.akey[w][0][0][0][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int chunk = lane + 64 * i;                 // 16-byte chunk of the wave's 4 KB
+      const int buf = chunk >> 7, row = (chunk >> 1) & 15;
+      const uint32_t v = row == 6 + 8 * buf ? 0xB8B8B8B8u : 0u;
+      *reinterpret_cast<uint4*>(ak + 16 * chunk) = make_uint4(v, v, v, v);
+    }
+  }
 
   // Row extent.
   int len = as_const(c.seq_lens)[b];
@@ -872,7 +968,6 @@ void decode_kernel(DecodeParams prm) {
   k.gated = BITS == 4 && d->gated != 0;
   k.scale2 = c.sm_scale * kLog2e;
   k.log2tau = c.tau > 0.f ? log2f(c.tau) : -INFINITY;
-  k.u = u;
   k.w = w;
   k.lane = lane;
   k.gs = gs;
@@ -922,15 +1017,16 @@ void decode_kernel(DecodeParams prm) {
   const int rounds = (ge - gs + 2 * NW - 1) / (2 * NW);
   const LaneOffs offs = lane_offsets<BITS, NVG, P>(lay, lane);
   PairRegs<BITS, NVG> regs;
-  LaneIds nid{0, 0};   // page ids of the next round's pair
+  int nid = 0;         // page ids of the next round's pair
   int pid_cur = 0;     // page holding the lane's token this round
   if (rounds > 0) {
     // the next round's ids go out before this round's data, as inside the loop
     const int gA = gs + 2 * w;
-    const LaneIds id0 = load_ids<P>(r, gA, ge, lane);
-    nid = load_ids<P>(r, gA + 2 * NW, ge, lane);
-    const PairPages pp = pair_pages<P>(r, id0);
-    load_keys<BITS, NVG>(regs, pp, offs);
+    const int id0 = load_pair_ids<P>(r, gA, ge, lane);
+    nid = load_pair_ids<P>(r, gA + 2 * NW, ge, lane);
+    const PairPages pp = pair_pages<P>(r, id0, lane);
+    load_kc<BITS, P, NVG>(regs, pp, offs);
+    regs.ksz = *gp<u32x4>(pp.ksz + offs.ksz);
     load_vsz<BITS, NVG>(regs, pp, offs);
     load_vc<BITS, NVG>(regs, pp, offs);
     pid_cur = pp.tok_pid;
@@ -941,7 +1037,7 @@ void decode_kernel(DecodeParams prm) {
     for (int i = 0; i < NW; ++i) st.m_run = dmax(st.m_run, sm.sink_max[i]);
   }
 
-  for (int rd = 0; rd < rounds; ++rd) round_body<BITS, NVG, P, NW>(sm, st, regs, pid_cur, nid, r, offs, k, rd);
+  for (int rd = 0; rd < rounds; ++rd) round_body<BITS, NVG, P, NW>(sm, st, regs, pid_cur, nid, r, k, rd);
   // Low planes of the last round.
   if (BITS == 4 && rounds > 0) add_prev_lo<NVG, NW>(sm, st, (rounds - 1) & 1, w, lane, k.mk);
 

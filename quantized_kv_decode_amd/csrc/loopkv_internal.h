@@ -6,16 +6,21 @@
 // block of a page of P tokens, D channels and NVG value groups:
 //
 //   KSZ  4*D          fp16 (scale, zero) per channel of the key group starting in this page
-//   KC   P*D*bits/8   key codes, 32-bit words W[cb][t] at word cb*P + t
-//                       INT4: channel 8*cb + i in bits 4i..4i+3
-//                       INT2: channel 16*cb + i in bits 2i..2i+1
+//   KC   P*D*bits/8   key codes, token-major 32-bit words W[t][w] at word t*(D*bits/32) + w
+//                       INT4: word w holds channels 8w..8w+7; channel 8w + i (i < 4) in bits
+//                             8i..8i+3, channel 8w + 4 + i in bits 8i+4..8i+7
+//                       INT2: word w holds channels 16w..16w+15; channel 16w + 4k + i
+//                             (k, i < 4) in bits 8i+2k..8i+2k+1
 //   VC   P*D/4        INT4 high plane / INT2 codes, W[cb][t] at word cb*P + t,
 //                       channel 16*cb + i in bits 2i..2i+1
 //   VSZ  4*P*NVG      fp16 (scale, zero) per (token, value group), token-major
 //   VLO  P*D/4        INT4 low plane, token-major W[t][cb] at word t*(D/16) + cb, so one
 //                       token's low plane is D/4 contiguous bytes
 //
-// Column-major code words give each lane of a wave contiguous 16-byte loads of several
+// Token-major key rows give each lane of a wave one contiguous load of 32 channels of one
+// token, the operand of the score MFMA: masking a key word's nibbles (or 2-bit fields) into
+// bytes leaves four consecutive channels per register, so the codes enter the MFMA with no
+// reordering. Column-major value words give each lane contiguous 16-byte loads of several
 // tokens of the same channels; the token-major low plane makes a hot token's fetch one
 // contiguous D/4-byte row.
 #pragma once

@@ -192,7 +192,13 @@ def _pack_pool_heads_reversed(bits, page_tokens, heads_q, page_table, num_pages,
     return M.__dict__["_orig_pack_pool"](bits, page_tokens, rev, page_table, num_pages, v_group, hist_start)
 
 
+def _kc_fields_in_channel_order(bits):
+    return np.arange(32 // bits)
+
+
 MUTANTS = {
+    "key-code words packed in plain channel order": ("_kc_field_channels", _kc_fields_in_channel_order,
+                                                     [P.test_layout_fixture_positions], []),
     "pool pages placed from token 0 despite a sink": ("pack_pool", _pack_pool_ignores_sink,
                                                       [P.test_pool_placement_fixture], []),
     "pool head blocks in reverse order": ("pack_pool", _pack_pool_heads_reversed,
