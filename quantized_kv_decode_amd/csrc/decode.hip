@@ -710,6 +710,15 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   wave_lds_sync();
 }
 
+// Device-scope coherent float store and load (relaxed atomics at agent scope): they bypass
+// the non-coherent per-XCD L2, so another workgroup on any XCD sees the stored value.
+__device__ __forceinline__ void store_device(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_device(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 struct DecodeParams {
   Geom g;
   DecodeCall c;
@@ -1100,8 +1109,8 @@ void decode_kernel(DecodeParams prm) {
       c.out[row * kHeadDim + tid] = den > 0.f ? num / den : 0.f;
     } else {
       float* part = c.partials + (row * g.max_splits + split) * (kHeadDim + 2);
-      part[2 + tid] = num;
-      if (tid == 0) { part[0] = Mx; part[1] = den; }
+      store_device(&part[2 + tid], num);
+      if (tid == 0) { store_device(&part[0], Mx); store_device(&part[1], den); }
     }
   }
   // Split partials: the workgroup that finishes a row group's last split merges them
@@ -1110,29 +1119,34 @@ void decode_kernel(DecodeParams prm) {
   if (c.n_split > 1) {
     __shared__ int s_last;
     int* counter = c.counters + (size_t)b * H + (int)blockIdx.y * RB;
-    __threadfence();   // this thread's partials reach the device before the count
+    // The partials went out as device-coherent stores; once they are complete (vmcnt 0) in
+    // every thread of the workgroup, the count is raised. No agent-scope fence: on this chip
+    // that writes back and invalidates the whole L2 of the XCD, in every wave.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (threadIdx.x == 0) s_last = atomicAdd(counter, 1) == c.n_split - 1;
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == c.n_split - 1;
     __syncthreads();
     if (s_last) {
-      __threadfence();   // the other workgroups' partials, not stale cached copies
+      // device-coherent loads: the other workgroups' partials, never a stale cached copy
       if (tid < kHeadDim) {
         const size_t row = (size_t)b * H + h;
         const float* base = c.partials + row * g.max_splits * (kHeadDim + 2);
         float Mx = -INFINITY;
-        for (int sp = 0; sp < c.n_split; ++sp) Mx = fmaxf(Mx, base[sp * (kHeadDim + 2)]);
+        for (int sp = 0; sp < c.n_split; ++sp) Mx = fmaxf(Mx, load_device(&base[sp * (kHeadDim + 2)]));
         float num = 0.f, den = 0.f;
         if (Mx != -INFINITY) {
           for (int sp = 0; sp < c.n_split; ++sp) {
             const float* pp = base + sp * (kHeadDim + 2);
-            const float fw = pp[0] == -INFINITY ? 0.f : exp2f(pp[0] - Mx);
-            num = fmaf(fw, pp[2 + tid], num);
-            den = fmaf(fw, pp[1], den);
+            const float m = load_device(&pp[0]);
+            const float fw = m == -INFINITY ? 0.f : exp2f(m - Mx);
+            num = fmaf(fw, load_device(&pp[2 + tid]), num);
+            den = fmaf(fw, load_device(&pp[1]), den);
           }
         }
         c.out[row * kHeadDim + tid] = den > 0.f ? num / den : 0.f;
       }
-      if (threadIdx.x == 0) *counter = 0;
+      if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (tid == 0 && c.stats) {
