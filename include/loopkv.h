@@ -266,9 +266,9 @@ loopkv_status loopkv_decode_attention_static(loopkv_plan plan, int32_t layer, in
 
 /* The split_tokens a decode with LOOPKV_SPLIT_AUTO uses for `batch` requests and a page table
  * of `page_table_stride` entries (context c = min(max_pages_per_seq, stride) * page_tokens):
- * n = min(ceil(4 * CUs / (batch * num_kv_heads)), 64, shape.max_splits, floor(c / 2048)) splits
+ * n = min(ceil(4 * CUs / (batch * num_kv_heads)), 64, shape.max_splits, floor(c / 1024)) splits
  * (enough that the rows fill every compute unit of the device with four rows' waves, at most
- * 64 far blocks per row as in section 3.4, none shorter than 2048 tokens); 0 (no split) when
+ * 64 far blocks per row as in section 3.4, none shorter than 1024 tokens); 0 (no split) when
  * n <= 1, else ceil(c / n) rounded up to a multiple of 32. Deterministic for a device, so a
  * caller (or a test) can reproduce the fetch mask. Host only. Errors: LOOPKV_EINVAL. */
 loopkv_status loopkv_auto_split(loopkv_plan plan, int32_t batch, int32_t page_table_stride,

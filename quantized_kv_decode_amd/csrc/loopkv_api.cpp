@@ -187,7 +187,7 @@ Geom make_geom(const loopkv_plan_s* p) {
 // splits fetch more low planes, and each split workgroup pays a fixed prologue and merge. At
 // most 64 splits per row (section 3.4: up to 64 far blocks per decode row) and max_splits.
 constexpr int64_t kAutoRowsPerCu = 4;
-constexpr int64_t kAutoMinSplit = 2048;
+constexpr int64_t kAutoMinSplit = 1024;
 
 int32_t auto_split(const loopkv_plan_s* p, int32_t batch, int64_t ctx) {
   const int64_t rows = (int64_t)batch * p->shape.num_kv_heads;

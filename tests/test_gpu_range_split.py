@@ -58,7 +58,7 @@ def test_decode_value_magnitudes(bits, scale):
 def _expected_auto_split(batch, heads, ctx, cus, max_splits):
     """The rule loopkv.h states for LOOPKV_SPLIT_AUTO."""
     rows = batch * heads
-    n = min(-(-4 * cus // rows), 64, max_splits, ctx // 2048)
+    n = min(-(-4 * cus // rows), 64, max_splits, ctx // 1024)
     if n <= 1:
         return 0
     return -(-(-(-ctx // n)) // 32) * 32
