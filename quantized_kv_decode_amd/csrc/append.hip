@@ -119,7 +119,7 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
   // The group's keys as their bf16 bits (rows 16-byte aligned): half the LDS of an fp32 tile, so
   // that more of a decode step's workgroups are resident at once.
   __shared__ __attribute__((aligned(16))) uint16_t ks[kGroup][kHeadDim + 8];
-  __shared__ uint8_t kcode[kGroup][kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint32_t kszs[kHeadDim];   // per channel: fp16 s | z << 16
   __shared__ int64_t page_base[kGroup / 16];
 
   const int H = g.H, D = g.D;   // D == kHeadDim (checked on the host)
@@ -244,44 +244,72 @@ __global__ __launch_bounds__(128) void quantize_group_kernel(
           (uint32_t)sb | ((uint32_t)zb << 16);
   }
 
-  // Keys: thread = channel; min/max over the group's tokens.
+  // Keys: thread = channel; min/max over the group's tokens (all 32 staged values read first).
   {
     const int c = tid;
-    float mnf = __uint_as_float((uint32_t)ks[0][c] << 16), mxf = mnf;
+    float x[kGroup];
+#pragma unroll
+    for (int tt = 0; tt < kGroup; ++tt) x[tt] = __uint_as_float((uint32_t)ks[tt][c] << 16);
+    float mnf = x[0], mxf = x[0];
+#pragma unroll
     for (int tt = 1; tt < kGroup; ++tt) {
-      const float x = __uint_as_float((uint32_t)ks[tt][c] << 16);
-      mnf = x < mnf ? x : mnf;
-      mxf = x > mxf ? x : mxf;
+      mnf = x[tt] < mnf ? x[tt] : mnf;
+      mxf = x[tt] > mxf ? x[tt] : mxf;
     }
     const double mn = mnf, mx = mxf;
     const uint16_t sb = f64_to_f16_bits((mx - mn) / (double)L);
     const uint16_t zb = f64_to_f16_bits(mn);
-    const double s = f16_bits_to_f64(sb), z = f16_bits_to_f64(zb);
-    const float s32 = (float)s, z32 = (float)z;   // exact: fp16 values
-    for (int tt = 0; tt < kGroup; ++tt)
-      kcode[tt][c] = (uint8_t)quant_code_fast(__uint_as_float((uint32_t)ks[tt][c] << 16), s32, z32, s, z, L);
+    const uint32_t szw = (uint32_t)sb | ((uint32_t)zb << 16);
+    kszs[c] = szw;
     uint8_t* blk = d.own_pool + page_base[0] + hoff;
-    reinterpret_cast<uint32_t*>(blk + lay.ksz)[c] = (uint32_t)sb | ((uint32_t)zb << 16);
+    reinterpret_cast<uint32_t*>(blk + lay.ksz)[c] = szw;
   }
   __syncthreads();
 
-  // Key code words, token-major W[t][w]: KPW channels of one token per word, in the field order
-  // that masking a word into bytes turns into four consecutive channels per 32-bit register
-  // (INT4: channel 8w + i in bits 8i..8i+3, 8w + 4 + i in bits 8i+4..8i+7; INT2: channel
-  // 16w + 4k + i in bits 8i+2k..8i+2k+1).
-  constexpr int KPW = 32 / BITS;
-  constexpr int NKW = kHeadDim / KPW;   // words per token
-  for (int w = tid; w < NKW * kGroup; w += 128) {
-    const int tt = w / NKW, cw = w % NKW;
-    uint32_t word = 0;
+  // Key codes of the thread's own token t, channels c0 .. c0 + 31 (still in registers from the
+  // staging loads), packed straight into its token-major words: KPW channels per word, in the
+  // field order that masking a word into bytes turns into four consecutive channels per 32-bit
+  // register (INT4: channel 8w + i in bits 8i..8i+3, 8w + 4 + i in bits 8i+4..8i+7; INT2:
+  // channel 16w + 4k + i in bits 8i+2k..8i+2k+1).
+  {
+    uint32_t szv[32];
 #pragma unroll
-    for (int f = 0; f < KPW; ++f) {
-      const int ch = BITS == 4 ? (f % 2) * 4 + f / 2 : 4 * (f % 4) + f / 4;
-      word |= (uint32_t)kcode[tt][cw * KPW + ch] << (BITS * f);
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&kszs[c0 + 4 * i]);
+      szv[4 * i] = v.x; szv[4 * i + 1] = v.y; szv[4 * i + 2] = v.z; szv[4 * i + 3] = v.w;
+    }
+    uint32_t code[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t w2 = kw[i / 8][(i % 8) / 2];
+      const float xv = __uint_as_float((i & 1) ? (w2 & 0xFFFF0000u) : (w2 << 16));
+      const float s32 = (float)__builtin_bit_cast(_Float16, (uint16_t)(szv[i] & 0xFFFFu));
+      const float z32 = (float)__builtin_bit_cast(_Float16, (uint16_t)(szv[i] >> 16));
+      code[i] = (uint32_t)quant_code_fast(xv, s32, z32, (double)s32, (double)z32, L);
+    }
+    constexpr int KPW = 32 / BITS;
+    constexpr int NKW = kHeadDim / KPW;   // words per token
+    constexpr int TW = 32 / KPW;          // words of the thread's 32 channels
+    uint32_t word[TW];
+#pragma unroll
+    for (int w = 0; w < TW; ++w) {
+      word[w] = 0;
+#pragma unroll
+      for (int f = 0; f < KPW; ++f) {
+        const int ch = BITS == 4 ? (f % 2) * 4 + f / 2 : 4 * (f % 4) + f / 4;
+        word[w] |= code[w * KPW + ch] << (BITS * f);
+      }
     }
     int tl;
-    uint8_t* blk = tok_block(tt, &tl);
-    reinterpret_cast<uint32_t*>(blk + lay.kc)[tl * NKW + cw] = word;
+    uint8_t* blk = tok_block(t, &tl);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(blk + lay.kc) + tl * NKW + part * TW;
+    if constexpr (TW == 4) {
+      u32x4 o;
+      o.x = word[0]; o.y = word[1]; o.z = word[2]; o.w = word[3];
+      *reinterpret_cast<u32x4*>(dst) = o;
+    } else {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(word[0], word[1]);
+    }
   }
 }
 

@@ -22,12 +22,14 @@ def _cells(w):
     return [(t, l) for t in range(w.T) for l in range(w.L)]
 
 
-@pytest.mark.parametrize("P,sink,window", [(32, 0, 0), (16, 32, 64)])
-def test_graph_replays_match_eager_step(P, sink, window):
+@pytest.mark.parametrize("P,sink,window,split", [(32, 0, 0, 0), (16, 32, 64, 0), (32, 0, 0, 64)])
+def test_graph_replays_match_eager_step(P, sink, window, split):
+    """split > 0: every decode is split, and the partials are merged inside the launch by the
+    row group's last workgroup, whose counters must be back at zero for every replay."""
     plan = np.array([[4, 2], [2, 4], [0, 0], [4, 2]], np.uint8)
     lens0 = np.array([31, 96, 170, 257, 33], np.int32)
     steps = 4
-    log(f"graph step P={P} sink={sink} window={window}")
+    log(f"graph step P={P} sink={sink} window={window} split={split}")
     ws = [Workload(plan, batch=5, lens=lens0 + steps + 1, page_tokens=P, seed=123, sink_tokens=sink,
                    window_tokens=window) for _ in range(2)]
     g_w, e_w = ws
@@ -61,7 +63,8 @@ def test_graph_replays_match_eager_step(P, sink, window):
     def step(w, x):
         for (t, l) in _cells(w):
             w.cache.append(l, t, x["k"][t, l], x["v"][t, l], x["before"], w.page_table)
-            w.cache.decode(l, t, q[t, l], x["after"], w.page_table, tau=tau, out=x["out"][t, l])
+            w.cache.decode(l, t, q[t, l], x["after"], w.page_table, tau=tau, split_tokens=split,
+                           out=x["out"][t, l])
 
     def advance(w):
         for c in _cells(w):
@@ -102,6 +105,6 @@ def test_graph_replays_match_eager_step(P, sink, window):
                 assert torch.equal(a, b), f"replay {r} ring"
         log(f"  replay {r} equal to the eager step")
     for (t, l) in _cells(g_w):
-        ref, _ = g_w.oracle_decode(t, l, q[t, l].cpu(), tau=tau)
+        ref, _ = g_w.oracle_decode(t, l, q[t, l].cpu(), tau=tau, split_tokens=split)
         check_out(io["g"]["out"][t, l], ref, f"graph cell {(t, l)}")
     assert g_w.cache.device_errors() == 0 and e_w.cache.device_errors() == 0
