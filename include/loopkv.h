@@ -228,7 +228,10 @@ loopkv_status loopkv_quantize_append(loopkv_plan plan, int32_t layer, int32_t lo
  * (tau 0, default scale, no split). Every call is one kernel launch, split or not.
  * Value range: any finite fp16 value scale (the weights are rescaled per wave by powers of
  * two, section 3.3 keeps a scale per group); exact (bf16) sink, window and tail values must
- * be below 2^118 in magnitude.
+ * be below 2^118 in magnitude. History scores are formed on the matrix cores from q * s_K
+ * rounded to 24 bits relative to the largest |q * s_K| of its 32-channel block (about fp32's
+ * precision for the score); in a block whose largest |q * s_K| is below 2^-110 the
+ * score's absolute error stays below 2^-100, and every q * s_K must be finite in fp32.
  * Workspace: the split partials and the merge counters are one region of the plan's arena,
  * so split decodes of one plan (split_tokens != 0) must not overlap in time: issue them on
  * one stream (or order the streams), as the calls of one model step are. Errors:
