@@ -122,3 +122,34 @@ def test_sink_window_split_reuse_repeats(split):
             w.check_masks(res[0][1], hot, t, 0, q, 0.02, split)
         log(f"  step {step} ok")
     assert w.cache.device_errors() == 0
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("kind", ["spread", "zero_blocks"])
+def test_decode_query_dynamic_range(bits, kind):
+    """The history scores' query operand is rounded relative to the largest |q * s_K| of each
+    32-channel block: queries whose channels span 10^-4 .. 10^1 (spread), or whose first and
+    third 32-channel blocks are exactly zero for some heads (zero_blocks), still give outputs
+    within 2e-3 of the oracle and its fetch masks."""
+    log(f"query dynamic range bits={bits} kind={kind}")
+    plan = np.array([[bits]], np.uint8)
+    w = Workload(plan, batch=3, lens=[900, 417, 1200], seed=91 + bits)
+    w.append_upto(w.lens, chunk=400)
+    q = synth.queries(3, 16, 128, 910 + bits).double()
+    g = torch.Generator().manual_seed(9 + bits)
+    if kind == "spread":
+        q = q * 10.0 ** (torch.rand(1, 1, 128, generator=g, dtype=torch.float64) * 5 - 4)
+        q = q * 4.0   # keep the scores' spread like the unscaled queries'
+    else:
+        q[:, ::2, 0:32] = 0.0
+        q[:, ::3, 64:96] = 0.0
+    q = q.to(torch.bfloat16)
+    for tau, split in [(0.01, 0), (0.02, 256)]:
+        mask = _mask_buf(w)
+        out = w.cache.decode(0, 0, q.cuda(), w.seq_lens(0, 0), w.page_table, tau=tau, split_tokens=split,
+                             fetch_mask=mask)
+        ref, hot = w.oracle_decode(0, 0, q, tau=tau, split_tokens=split)
+        err = check_out(out, ref, f"bits {bits} {kind} tau {tau} split {split}")
+        w.check_masks(mask, hot, 0, 0, q, tau, split)
+        log(f"  tau {tau} split {split}: relative error {err:.2e}")
+    assert w.cache.device_errors() == 0
