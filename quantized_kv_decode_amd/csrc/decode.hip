@@ -36,9 +36,9 @@
 //    into the query, per group and channel) written as a 24-bit integer relative to the
 //    largest magnitude of its 32-channel scale block, offset by 2^23 and split into six
 //    base-16 digits (rows of fp8 integers 0..15), plus a constant row that removes the offset;
-//    each row and block carries its power of two in the MFMA's E8M0 block scale. Every product and block
-//    sum is exact, so the score keeps fp32 accuracy (22 bits of q * s_K per block) and the
-//    hot/cold test sees fp32-accurate scores. The key zero point enters as the accumulator's
+//    each row and block carries its power of two in the MFMA's E8M0 block scale. Every
+//    product and block sum is exact, so the score keeps fp32 accuracy (22 bits of q * s_K per
+//    block) and the hot/cold test sees fp32-accurate scores. The key zero point enters as the accumulator's
 //    initial value (sum over channels of q * z_K).
 //  - values (INT4 high plane, INT2 codes): two tokens' words are interleaved with one byte
 //    permute so each 16-bit half holds one token's channels; a code moved to mantissa bits 4..9
