@@ -872,7 +872,7 @@ __device__ __forceinline__ void exact_chunk(Smem<NVG, NW>& sm, WaveState<NVG>& s
 constexpr int kMaxOrderBatch = 1024;   // larger batches keep the launch order
 
 template <int BITS, int NVG, int P, int NW, int RB>
-__global__ __launch_bounds__(64 * NW * RB) __attribute__((amdgpu_waves_per_eu(NW, NW)))
+__global__ __launch_bounds__(64 * NW * RB) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 4, NW == 8 ? 2 : 4)))
 void decode_kernel(DecodeParams prm) {
   const Geom& g = prm.g;
   const DecodeCall& c = prm.c;
@@ -1160,9 +1160,11 @@ void decode_kernel(DecodeParams prm) {
   }
 }
 
-// Waves per (request, head) row, which is also the waves per SIMD the register allocation
-// targets: with four rows per workgroup, one workgroup fills a CU at four waves per SIMD
-// (128 VGPRs).
+// Waves per (request, head) row. With four rows per workgroup, one workgroup fills a CU at
+// four waves per SIMD (128 VGPRs). One-row workgroups take eight waves (two per SIMD, up to
+// 256 VGPRs) when the launch is a single generation of workgroups with splits of at least 1024
+// tokens: a small launch (few requests, so split rows) then runs half as many rounds per
+// workgroup, which is its latency.
 #ifndef LOOPKV_NW2
 #define LOOPKV_NW2 4
 #endif
@@ -1170,18 +1172,17 @@ void decode_kernel(DecodeParams prm) {
 #define LOOPKV_NW4 4
 #endif
 
-template <int BITS, int P, int RB>
-hipError_t launch_bpr(const Geom& g, const DecodeCall& c, hipStream_t stream) {
+template <int BITS, int P, int RB, int NW>
+hipError_t launch_bprw(const Geom& g, const DecodeCall& c, hipStream_t stream) {
   DecodeParams prm{g, c};
   const dim3 grid((unsigned)c.n_split, (unsigned)(g.H / RB), (unsigned)c.batch);
   // one workgroup fills a CU
   prm.c.order_by_len = (int64_t)grid.x * grid.y * grid.z > (int64_t)g.cus;
-  constexpr int kNW = BITS == 2 ? LOOPKV_NW2 : LOOPKV_NW4;
-  const unsigned threads = 64 * kNW * RB;
+  const unsigned threads = 64 * NW * RB;
   switch (g.nvg) {
-    case 1: decode_kernel<BITS, 1, P, kNW, RB><<<grid, threads, 0, stream>>>(prm); break;
-    case 2: decode_kernel<BITS, 2, P, kNW, RB><<<grid, threads, 0, stream>>>(prm); break;
-    case 4: decode_kernel<BITS, 4, P, kNW, RB><<<grid, threads, 0, stream>>>(prm); break;
+    case 1: decode_kernel<BITS, 1, P, NW, RB><<<grid, threads, 0, stream>>>(prm); break;
+    case 2: decode_kernel<BITS, 2, P, NW, RB><<<grid, threads, 0, stream>>>(prm); break;
+    case 4: decode_kernel<BITS, 4, P, NW, RB><<<grid, threads, 0, stream>>>(prm); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1193,8 +1194,13 @@ hipError_t launch_bpr(const Geom& g, const DecodeCall& c, hipStream_t stream) {
 template <int BITS, int P>
 hipError_t launch_bp(const Geom& g, const DecodeCall& c, hipStream_t stream) {
   const int64_t wg4 = (int64_t)c.n_split * (g.H / 4) * c.batch;
-  return g.H % 4 == 0 && wg4 >= g.cus ? launch_bpr<BITS, P, 4>(g, c, stream)
-                                       : launch_bpr<BITS, P, 1>(g, c, stream);
+  if (g.H % 4 == 0 && wg4 >= g.cus)
+    return launch_bprw<BITS, P, 4, BITS == 2 ? LOOPKV_NW2 : LOOPKV_NW4>(g, c, stream);
+  const int64_t wg1 = (int64_t)c.n_split * g.H * c.batch;
+  const int64_t span = c.n_split > 1 ? (int64_t)c.split_tokens
+                                     : std::min<int64_t>(g.max_ctx, (int64_t)c.pt_stride * P);
+  if (wg1 <= g.cus && span >= 32 * kGroup) return launch_bprw<BITS, P, 1, 8>(g, c, stream);
+  return launch_bprw<BITS, P, 1, 4>(g, c, stream);
 }
 
 }  // namespace
