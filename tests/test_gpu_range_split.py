@@ -153,3 +153,23 @@ def test_decode_query_dynamic_range(bits, kind):
         w.check_masks(mask, hot, 0, 0, q, tau, split)
         log(f"  tau {tau} split {split}: relative error {err:.2e}")
     assert w.cache.device_errors() == 0
+
+
+def test_decode_max_splits():
+    """The largest split count a row can take (64 splits of 32 tokens; the shorter request's last
+    splits are empty), against the oracle for a 4-bit, a 2-bit and a reusing cell: every split's
+    partials meet in the in-launch merge."""
+    log("max splits")
+    plan = np.array([[4], [2], [0], [4]], np.uint8)
+    lens = np.array([2048, 1500], np.int32)
+    w = Workload(plan, batch=2, lens=lens, seed=131, max_splits=64)
+    w.append_upto(lens, chunk=512)
+    seq = torch.as_tensor(lens).cuda()
+    for t in range(4):
+        q = synth.queries(2, 16, 128, 1310 + t)
+        mask = _mask_buf(w)
+        out = w.cache.decode(0, t, q.cuda(), seq, w.page_table, tau=0.01, split_tokens=32, fetch_mask=mask)
+        ref, hot = w.oracle_decode(t, 0, q, tau=0.01, split_tokens=32)
+        check_out(out, ref, f"loop {t} split 32")
+        w.check_masks(mask, hot, t, 0, q, 0.01, 32)
+    assert w.cache.device_errors() == 0
