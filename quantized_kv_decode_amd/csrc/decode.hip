@@ -571,8 +571,11 @@ __device__ __forceinline__ void round_body(Smem<NVG, NW>& sm, WaveState<NVG>& st
   const float gmA = dmax(lane_f(rm, 0), lane_f(rm, 16));
   const float gmB = dmax(lane_f(rm, 32), lane_f(rm, 48));
   // Running maximum before each of the wave's two groups (4-bit history only: 2-bit history
-  // has no low plane to gate, and its waves need not wait for each other).
+  // has no low plane to gate). The 2-bit waves still meet once per round: in lockstep the
+  // workgroup's waves stream neighbouring head blocks of the same pages together, which
+  // measured 1-2% faster than letting them drift apart.
   float mpreA = 0.f, mpreB = 0.f;
+  if (BITS == 2) __syncthreads();
   if (BITS == 4) {
     if (lane == 0) {
       sm.gmax[rd & 1][w][0] = gmA;
