@@ -330,7 +330,7 @@ __device__ __forceinline__ void load_kc(PairRegs<BITS, NVG>& g, const PairPages&
   for (int k = 0; k < 4; ++k) {
     // with 32-token pages the second tile of a group is 16 rows further in the same page
     const gbytes a = pp.kt[k] + o.kc + (P == kGroup && (k & 1) ? 16 * ROW : 0);
-    if (BITS == 4) {
+    if constexpr (BITS == 4) {
       const u32x4 v = *gp<u32x4>(a);
       g.kc[k][0] = v.x; g.kc[k][1] = v.y; g.kc[k][2] = v.z; g.kc[k][3] = v.w;
     } else {
