@@ -63,7 +63,6 @@ constexpr float kWInit = 16777216.f;     // 2^24
 constexpr float kWMax = 32768.f;         // 2^15: largest K * s
 constexpr float kWExact = 256.f;         // 2^8: largest K while exact tokens are added
 
-typedef float float2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -91,11 +90,6 @@ __device__ __forceinline__ float f16_lo(uint32_t w) {
 }
 __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
-}
-// Bytes 0,1 (HI = false) or 2,3 (HI = true) of w as fp8 -> two floats.
-template <bool HI>
-__device__ __forceinline__ float2v cvt2(uint32_t w) {
-  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
 }
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float dot2(half2v a, uint32_t b, float c) {
@@ -246,15 +240,8 @@ __device__ __forceinline__ int load_pair_ids(const RowCtx& r, int g, int ge, int
   return r.pt_row[gg * PPG + j % PPG];
 }
 
-// A page id outside the pool is reported and replaced by page 0.
-__device__ __forceinline__ int checked_page(const RowCtx& r, int pid) {
-  if ((uint32_t)pid >= r.num_pages) {
-    atomicOr(r.err, (uint32_t)kErrPage);
-    pid = 0;
-  }
-  return pid;
-}
-// The same for a wave-uniform id: one lane reports.
+// A page id outside the pool is reported (by one lane: the id is wave-uniform) and replaced
+// by page 0.
 __device__ __forceinline__ int checked_page_u(const RowCtx& r, int pid, int lane) {
   if ((uint32_t)pid >= r.num_pages) {
     if (lane == 0) atomicOr(r.err, (uint32_t)kErrPage);
@@ -879,8 +866,6 @@ __global__ __launch_bounds__(64 * NW * RB) __attribute__((amdgpu_waves_per_eu(NW
 void decode_kernel(DecodeParams prm) {
   const Geom& g = prm.g;
   const DecodeCall& c = prm.c;
-  constexpr int KCH = 32 / BITS;
-  constexpr int NCB = kHeadDim / KCH;
   constexpr float VS = BITS == 4 ? 4.f : 1.f;   // value units of acc: true = VS * code
   static_assert(NW >= 2, "the final merge uses 128 threads");
   // RB rows (heads of one request) per workgroup, NW waves each, one workgroup per CU: with
