@@ -114,3 +114,28 @@ def test_short_rows_sink_only():
     assert s[0] == 0 and s[3] == 16 * (7 + 32 + 250)
     assert w.cache.qgroups(0, 0).cpu().numpy().tolist() == [1, 1, 1, 1]
     assert w.cache.device_errors() == 0
+
+
+def test_sink_window_eight_wave_rows():
+    """A small launch of long rows (2 requests, one head per workgroup, eight waves per row:
+    the launch is a single generation and each split spans at least 1024 tokens) with a sink
+    and a window: unsplit, 1024-token splits and the automatic split, against the oracle and
+    its fetch masks, for a 4-bit, a 2-bit and a reusing cell."""
+    plan = np.array([[4], [2], [0], [4]], np.uint8)
+    lens = np.array([2300, 1450], np.int32)
+    w = Workload(plan, batch=2, lens=lens, seed=141, sink_tokens=32, window_tokens=256)
+    w.append_upto(lens, chunk=700)
+    seq = torch.as_tensor(lens).cuda()
+    auto = w.cache.auto_split(2, w.page_table)
+    assert auto >= 1024, auto
+    for t in range(4):
+        q = synth.queries(2, 16, 128, 1410 + t)
+        for split in (0, 1024, L.SPLIT_AUTO):
+            ref_split = auto if split == L.SPLIT_AUTO else split
+            mask = _mask_buf(w)
+            out = w.cache.decode(0, t, q.cuda(), seq, w.page_table, tau=0.01, split_tokens=split,
+                                 fetch_mask=mask)
+            ref, hot = w.oracle_decode(t, 0, q, tau=0.01, split_tokens=ref_split)
+            check_out(out, ref, f"loop {t} split {split}")
+            w.check_masks(mask, hot, t, 0, q, 0.01, ref_split)
+    assert w.cache.device_errors() == 0
