@@ -45,3 +45,27 @@ def test_static_workspace_decode_matches_arena_decode():
         w2.cache.decode(0, 0, q, w2.seq_lens(0, 0), w2.page_table, tau=0.02, split_tokens=32,
                         static_workspace=True)
     assert e.value.status == L.ECAPACITY
+
+
+def test_static_workspace_small_launch():
+    """A small launch (one request, automatic split: two 1024-token splits in one-head
+    workgroups of eight waves) through the fixed array equals the arena entry point and the
+    oracle."""
+    plan = np.array([[4], [0], [4]], np.uint8)
+    lens = np.array([2040], np.int32)
+    w = Workload(plan, batch=1, lens=lens, seed=99, max_splits=64)
+    w.append_upto(w.lens, chunk=1024)
+    split = w.cache.auto_split(1, w.page_table)
+    assert split >= 1024, split
+    for t in range(3):
+        q = synth.queries(1, 16, 128, 990 + t)
+        seq = w.seq_lens(t, 0)
+        m_ref, m_st = _mask_buf(w, 1), _mask_buf(w, 1)
+        ref = w.cache.decode(0, t, q.cuda(), seq, w.page_table, tau=0.01, split_tokens=L.SPLIT_AUTO,
+                             fetch_mask=m_ref)
+        got = w.cache.decode(0, t, q.cuda(), seq, w.page_table, tau=0.01, split_tokens=L.SPLIT_AUTO,
+                             fetch_mask=m_st, static_workspace=True)
+        assert torch.equal(got, ref) and torch.equal(m_st, m_ref), t
+        orc, _ = w.oracle_decode(t, 0, q, tau=0.01, split_tokens=split)
+        check_out(got, orc, f"static workspace small launch loop {t}")
+    assert w.cache.device_errors() == 0
