@@ -877,7 +877,11 @@ void decode_kernel(DecodeParams prm) {
   const int rsub = wave / NW;
   Smem<NVG, NW>& sm = sm_rows[rsub];
   const int w = wave - rsub * NW;
-  const int split = blockIdx.x, h = blockIdx.y * RB + rsub;
+  // The dispatcher deals workgroups to the XCDs round-robin by linear index, so with the split
+  // as the fastest grid index an XCD would get the same split of every request (with ragged
+  // lengths, all the empty or all the full ones). The split is rotated by the request's
+  // position instead, so every XCD sees every split.
+  const int split = (int)((blockIdx.x + blockIdx.z) % gridDim.x), h = blockIdx.y * RB + rsub;
   const int tid = (int)threadIdx.x - rsub * 64 * NW;   // thread index among the row's waves
   const int lane = tid & 63;
   const LKV_CONST CellDesc* d = as_const(c.desc_dev);
