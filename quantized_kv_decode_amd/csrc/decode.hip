@@ -38,8 +38,8 @@
 //    base-16 digits (rows of fp8 integers 0..15), plus a constant row that removes the offset;
 //    each row and block carries its power of two in the MFMA's E8M0 block scale. Every
 //    product and block sum is exact, so the score keeps fp32 accuracy (22 bits of q * s_K per
-//    block) and the hot/cold test sees fp32-accurate scores. The key zero point enters as the accumulator's
-//    initial value (sum over channels of q * z_K).
+//    block) and the hot/cold test sees fp32-accurate scores. The key zero point enters as the
+//    accumulator's initial value (sum over channels of q * z_K).
 //  - values (INT4 high plane, INT2 codes): two tokens' words are interleaved with one byte
 //    permute so each 16-bit half holds one token's channels; a code moved to mantissa bits 4..9
 //    and OR-ed with the exponent of 1.0 is the fp16 number 1 + c/64, 1 + c/16 or 1 + c/4, and one
@@ -397,7 +397,7 @@ constexpr int kCodeScale = 127 + 9;   // E8M0 2^9: a code c in an fp8 byte is c 
 template <int BITS>
 __device__ __forceinline__ v8i spread_codes(const uint32_t (&w)[BITS == 4 ? 4 : 2]) {
   v8i b;
-  if (BITS == 4) {
+  if constexpr (BITS == 4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       b[2 * j] = (int)(w[j] & 0x0F0F0F0Fu);
